@@ -1,0 +1,358 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU needed).
+
+Each test checks the oracle against something it does not compute itself:
+values the pages print (``tests/golden``), hand-worked tables, closed forms,
+a brute-force definition checker (``defcheck``), and torch's own FP8 casts.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import defcheck
+import oracle
+import workloads
+
+FMTS = ("e4m3fn", "e5m2", "e2m1")
+INS = ("bf16", "f16")
+
+
+def _golden_constants():
+    return {k: v for k, v in defcheck.read_table("page_constants.txt")}
+
+
+# ---------------------------------------------------------------- page facts
+
+def test_emax_table_matches_page():
+    c = _golden_constants()
+    for fmt in FMTS:
+        assert oracle.emax(fmt) == int(c["emax." + fmt])
+
+
+def test_fp8_maxima_match_page():
+    c = _golden_constants()
+    for fmt in ("e4m3fn", "e5m2", "e2m1"):
+        code = int(c["maxcode." + fmt], 16)
+        val = float(c["maxval." + fmt])
+        assert oracle.narrow(np.array([val], np.float32), fmt)[0] == code
+        assert oracle.decode(np.array([code], np.uint8), fmt)[0] == val
+        # anything larger saturates to the same code, with its sign
+        big = np.array([val * 1.01, val * 1000, np.inf, -val * 3, -np.inf], np.float32)
+        sb = 0x8 if fmt == "e2m1" else 0x80
+        assert list(oracle.narrow(big, fmt)) == [code, code, code, code | sb, code | sb]
+
+
+def test_e2m1_grid_matches_page():
+    for nib, val in defcheck.read_table("e2m1_grid.txt"):
+        n = int(nib, 16)
+        v = float(val)
+        got = oracle.decode(np.array([n], np.uint8), "e2m1")[0]
+        assert got == v and math.copysign(1, got) == math.copysign(1, v)
+        assert oracle.encode_e2m1(v) == n
+
+
+def test_e2m1_hand_worked_ties():
+    for val, code in defcheck.read_table("e2m1_rne_ties.txt"):
+        assert oracle.encode_e2m1(float(val)) == int(code, 16), val
+
+
+def test_e4m3fn_hand_worked_ties():
+    for val, code in defcheck.read_table("e4m3fn_rne_ties.txt"):
+        assert oracle.narrow(np.array([float(val)], np.float32), "e4m3fn")[0] == int(code, 16), val
+
+
+def test_e8m0_clamps_match_page():
+    c = _golden_constants()
+    # all-zero (or all-denormal) block: max exponent byte 0 -> E8M0 1
+    for fmt in FMTS:
+        assert oracle.e8m0(0, oracle.emax(fmt)) == int(c["all_zero_block_e8m0"])
+        # CLAMP-LOW then ZERO-FLOOR: anything at or below the bias gives 1
+        for m in range(0, oracle.emax(fmt) + 2):
+            assert oracle.e8m0(m, oracle.emax(fmt)) == 1
+        for m in range(oracle.emax(fmt) + 1, 256):
+            assert oracle.e8m0(m, oracle.emax(fmt)) == m - oracle.emax(fmt)
+
+
+def test_prescale_is_power_of_two():
+    c = _golden_constants()
+    # E8M0 127 multiplies by exactly one
+    x = workloads.bf16_bits_to_f32(np.arange(0, 0x7F80, 7, dtype=np.uint16))
+    unit = int(c["unit_scale_e8m0"])
+    assert np.array_equal(oracle.prescale(x, np.uint8(unit)).view(np.uint32), x.view(np.uint32))
+    # the multiplier is 2^(127 - E8M0) for every reachable E8M0
+    e = np.arange(1, 254, dtype=np.uint8)
+    got = oracle.prescale(np.ones(e.size, np.float32), e).astype(np.float64)
+    assert np.array_equal(got, np.ldexp(1.0, 127 - e.astype(np.int64)))
+
+
+# ------------------------------------------------------------ widen (library)
+
+def test_f16_widen_matches_numpy_all_patterns():
+    h = np.arange(65536, dtype=np.uint16)
+    got = oracle.widen(h, "f16")
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_bf16_widen_all_patterns():
+    h = np.arange(65536, dtype=np.uint16)
+    got = oracle.widen(h, "bf16")
+    ref = torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# ----------------------------------------------- narrow: exhaustive + library
+
+def _reachable_products(in_dtype: str):
+    """Every finite input pattern times every prescale 2^(127-e), e in [1, 253],
+    as fp32 (what the oracle narrows) and exactly (float64)."""
+    h = np.arange(65536, dtype=np.uint16)
+    x = defcheck.widen(h, in_dtype)
+    x = x[np.isfinite(x)]
+    e = np.arange(1, 254)
+    exact = (x[None, :] * np.ldexp(1.0, 127 - e)[:, None]).ravel()
+    with np.errstate(over="ignore"):      # unreachable huge pairs become inf: both saturate
+        return exact.astype(np.float32), exact
+
+
+@pytest.mark.parametrize("in_dtype", INS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_narrow_exhaustive_vs_bruteforce(in_dtype, fmt):
+    y32, exact = _reachable_products(in_dtype)
+    got = oracle.narrow(y32, fmt)
+    # the same fp32 value through the brute-force nearest-code search
+    assert np.array_equal(got, defcheck.narrow_bruteforce(y32.astype(np.float64), fmt))
+    # and the exact product: rounding the product to fp32 first never
+    # changes the code (double rounding is harmless for a power-of-two scale)
+    assert np.array_equal(got, defcheck.narrow_bruteforce(exact, fmt))
+
+
+@pytest.mark.parametrize("in_dtype", INS)
+@pytest.mark.parametrize("fmt,tdtype,maxval", [("e4m3fn", torch.float8_e4m3fn, 448.0),
+                                                ("e5m2", torch.float8_e5m2, 57344.0)])
+def test_fp8_narrow_vs_torch_cast(in_dtype, fmt, tdtype, maxval):
+    """torch's CPU float8 casts round to nearest-even but do not saturate, so
+    clamping first gives the saturating narrow for finite inputs."""
+    y32, _ = _reachable_products(in_dtype)
+    t = torch.from_numpy(y32).clamp(-maxval, maxval).to(tdtype).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.narrow(y32, fmt), t)
+
+
+def test_fp8_decode_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt, tdt in (("e4m3fn", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        ref = torch.from_numpy(codes.copy()).view(tdt).double().numpy()
+        got = oracle.decode(codes, fmt)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e2m1_narrow_dense_fp32_range():
+    """Every fp32 pattern with magnitude in [2^-3, 2^4) (all of e2m1's rounding
+    boundaries), plus random patterns over the whole fp32 range."""
+    lo = np.float32(0.125).view(np.uint32)
+    hi = np.float32(16.0).view(np.uint32)
+    for start in range(int(lo), int(hi), 1 << 23):
+        u = np.arange(start, min(start + (1 << 23), int(hi)), dtype=np.uint32)
+        y = u.view(np.float32)
+        assert np.array_equal(oracle.narrow(y, "e2m1"), defcheck.narrow_bruteforce(y, "e2m1"))
+    rng = np.random.default_rng(11)
+    u = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    y = u.view(np.float32)
+    assert np.array_equal(oracle.narrow(y, "e2m1"), defcheck.narrow_bruteforce(y, "e2m1"))
+
+
+@pytest.mark.parametrize("fmt", ("e4m3fn", "e5m2"))
+def test_fp8_narrow_random_fp32(fmt):
+    rng = np.random.default_rng(12)
+    u = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    y = u.view(np.float32)
+    assert np.array_equal(oracle.narrow(y, fmt), defcheck.narrow_bruteforce(y, fmt))
+
+
+def test_nan_becomes_signed_zero():
+    y = np.array([np.nan, -np.nan], np.float32)
+    y[1] = -abs(y[1])
+    assert list(oracle.narrow(y, "e2m1")) == [0x0, 0x8]
+    assert list(oracle.narrow(y, "e4m3fn")) == [0x00, 0x80]
+    assert list(oracle.narrow(y, "e5m2")) == [0x00, 0x80]
+
+
+# ------------------------------------------------------------ E8M0 closed form
+
+@pytest.mark.parametrize("in_dtype", INS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_e8m0_bit_trick_equals_closed_form(in_dtype, fmt):
+    x = workloads.random_bits(64, 256, in_dtype, seed=21, specials=True)
+    _, image = oracle.quantize(x, in_dtype, fmt)
+    logical = image[defcheck.scale_slot(np.arange(64 // 8))]
+    absmax = np.abs(defcheck.widen(x, in_dtype)).reshape(8, 8, 64, 4).max(axis=(1, 3))
+    assert np.array_equal(logical, defcheck.e8m0_closed_form(absmax, fmt))
+
+
+def test_e8m0_range_for_finite_blocks():
+    for fmt in FMTS:
+        x = workloads.random_bits(128, 512, "bf16", seed=22)
+        _, image = oracle.quantize(x, "bf16", fmt)
+        logical = image[defcheck.scale_slot(np.arange(16))]
+        assert logical.min() >= 1 and logical.max() <= 254 - oracle.emax(fmt)
+
+
+def test_block_max_exponent_is_sign_blind_and_denormal_zero():
+    x = np.zeros((8, 4), np.float32)
+    x[3, 2] = -3.0                      # biased exponent 128
+    assert oracle.block_max_exponent(x, 0, 0) == 128
+    x[:] = np.float32(1e-40)            # fp32 denormals read exponent 0
+    assert oracle.block_max_exponent(x, 0, 0) == 0
+
+
+# ------------------------------------------------------- packing and placement
+
+def test_lane_remap_golden_and_involution():
+    for k, r, _byte, _hi in defcheck.read_table("fp4_container_order.txt"):
+        for q in range(5):
+            assert oracle.lane_remap(4 * q + int(k), 2) == 4 * q + int(r)
+    for stride in (1, 2, 3, 4, 8):
+        for i in range(200):
+            assert oracle.lane_remap(oracle.lane_remap(i, stride), stride) == i
+    assert [oracle.lane_remap(i, 1) for i in range(32)] == list(range(32))
+
+
+def test_scale_slot_golden_and_properties():
+    for i, s in defcheck.read_table("scale_slots.txt"):
+        assert oracle.scale_slot(int(i)) == int(s)
+        assert defcheck.scale_slot(int(i)) == int(s)
+    for P in (8, 16, 24, 32, 40, 64, 96, 128, 1024):
+        slots = [oracle.scale_slot(i) for i in range(P // 8)]
+        assert len(set(slots)) == len(slots) and max(slots) < P
+    # a 32-row shard's slots are the whole tensor's shifted by 8 rows per group
+    for i0 in range(0, 64, 4):
+        for k in range(12):
+            assert oracle.scale_slot(i0 + k) == oracle.scale_slot(k) + 8 * i0
+
+
+def test_fp4_container_bytes_hand_worked():
+    # one container per row: elements 0.5, 1, 1.5, 2 (codes 1, 2, 3, 4) at E8M0 127
+    # -> byte0 = e2 | e3 << 4 = 0x43, byte1 = e0 | e1 << 4 = 0x21 (golden table)
+    x = np.zeros((8, 4), np.uint16)
+    vals = np.array([0.5, 1.0, 1.5, 2.0], np.float32)
+    x[:] = workloads.f32_to_bf16_bits(vals)
+    x[0, 0] = workloads.f32_to_bf16_bits(np.array([4.0], np.float32))[0]   # pilot: exp 129 -> E8M0 127
+    data, image = oracle.quantize(x, "bf16", "e2m1")
+    assert image[0, 0] == 127
+    assert list(data[1]) == [0x43, 0x21]
+    assert list(data[0]) == [0x43, 0x26]      # element 0 is 4.0 -> code 6
+
+
+# ----------------------------------------------------- end to end, brute force
+
+@pytest.mark.parametrize("in_dtype", INS)
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("P,F", [(8, 4), (16, 8), (32, 12), (40, 8), (40, 12), (64, 36)])
+def test_oracle_equals_definitions_tiny(in_dtype, fmt, P, F):
+    for seed in range(3):
+        x = workloads.random_bits(P, F, in_dtype, seed=100 + seed, specials=True)
+        fill = np.full((P, F // 4), 0xA5, np.uint8)
+        d_or, im_or = oracle.quantize(x, in_dtype, fmt, image=fill)
+        d_df, im_df = defcheck.quantize(x, in_dtype, fmt, image=fill)
+        assert np.array_equal(d_or, d_df)
+        assert np.array_equal(im_or, im_df)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_oracle_equals_definitions_alt_emax(fmt):
+    x = workloads.random_bits(64, 64, "bf16", seed=31)           # finite inputs
+    d_or, im_or = oracle.quantize(x, "bf16", fmt, alt_emax=True)
+    d_df, im_df = defcheck.quantize(x, "bf16", fmt, alt=True)
+    assert np.array_equal(d_or, d_df) and np.array_equal(im_or, im_df)
+
+
+# -------------------------------------------------------------- properties
+
+@pytest.mark.parametrize("in_dtype", INS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_roundtrip_error_bound(in_dtype, fmt):
+    """decode(q) * 2^(e-127) is within half a grid step of x unless x
+    saturated, where it is +-max * 2^(e-127)."""
+    P, F = 64, 128
+    x = workloads.random_bits(P, F, in_dtype, seed=41)
+    data, image = oracle.quantize(x, in_dtype, fmt)
+    back = oracle.dequantize(data, image, P, F, fmt).astype(np.float64)
+    v = defcheck.widen(x, in_dtype)
+    e = np.repeat(np.repeat(image[defcheck.scale_slot(np.arange(P // 8))], 8, 0), 4, 1).astype(np.int64)
+    y = v * np.ldexp(1.0, 127 - e)
+    f = defcheck.FORMATS[fmt]
+    maxval = defcheck.code_values(fmt)[-1]
+    ay = np.abs(y)
+    sat = ay >= maxval
+    emin = 1 - f["bias"]
+    binade = np.floor(np.log2(np.where(ay > 0, ay, 1.0)))
+    step = np.ldexp(1.0, (np.maximum(binade, emin) - f["mbits"]).astype(np.int64))
+    err = np.abs(back.astype(np.float64) * np.ldexp(1.0, 127 - e) - y)
+    assert np.all(err[~sat] <= step[~sat] / 2)
+    assert np.all(np.abs(back[sat]) == maxval * np.ldexp(1.0, e[sat] - 127))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_prescaled_block_max_bounds(fmt):
+    """Before the narrow the prescaled block max is below 2^(EMAX+1); after it
+    every decoded magnitude is at most the format's largest value."""
+    P, F = 128, 256
+    x = workloads.random_bits(P, F, "bf16", seed=42)
+    data, image = oracle.quantize(x, "bf16", fmt)
+    e = np.repeat(np.repeat(image[defcheck.scale_slot(np.arange(P // 8))], 8, 0), 4, 1).astype(np.int64)
+    y = defcheck.widen(x, "bf16") * np.ldexp(1.0, 127 - e)
+    assert np.abs(y).max() < 2.0 ** (oracle.emax(fmt) + 1)
+    if fmt == "e2m1":
+        back = oracle.dequantize(data, image, P, F, fmt) * np.ldexp(1.0, 127 - e)
+    else:
+        back = oracle.decode(data, fmt)
+    assert np.abs(back).max() <= defcheck.code_values(fmt)[-1]
+
+
+def test_handplaced_workload_blocks():
+    x = workloads.handplaced_bf16_128x512()
+    data, image = oracle.quantize(x, "bf16", "e4m3fn")
+    logical = image[defcheck.scale_slot(np.arange(16))]
+    g, c = workloads.HANDPLACED["zero"]
+    assert logical[g, c] == 1
+    blk = data.reshape(16, 8, 128, 4)[g, :, c, :]
+    assert set(blk.ravel().tolist()) == {0x00, 0x80} and (blk == 0x80).sum() == 1
+    g, c = workloads.HANDPLACED["ties"]
+    assert logical[g, c] == 127
+    ties = {int(np.float32(float(v)).view(np.uint32)): int(code, 16)
+            for v, code in defcheck.read_table("e4m3fn_rne_ties.txt")}
+    vals = workloads.bf16_bits_to_f32(x.reshape(16, 8, 128, 4)[g, :, c, :]).ravel()
+    codes = data.reshape(16, 8, 128, 4)[g, :, c, :].ravel()
+    seen = 0
+    for v, code in zip(vals.view(np.uint32), codes):
+        if int(v) in ties:
+            assert code == ties[int(v)], hex(int(v))
+            seen += 1
+    assert seen == 29          # pilot + 28 tie values (the three +0.0 fillers are not listed)
+    g, c = workloads.HANDPLACED["outlier"]
+    assert logical[g, c] == 147 - 8          # 2^20 has biased exponent 147
+    g, c = workloads.HANDPLACED["subnormal"]
+    assert logical[g, c] == 1
+    # bf16 subnormal m * 2^-133 scaled by 2^126 is m * 2^-7: nonzero codes
+    sub = data.reshape(16, 8, 128, 4)[g, :, c, :]
+    assert np.all(sub & 0x7F > 0)
+
+
+def test_bad_shapes_rejected():
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((12, 8), np.uint16), "bf16", "e4m3fn")
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((8, 6), np.uint16), "bf16", "e4m3fn")
+
+
+def test_empty_is_noop():
+    d, im = oracle.quantize(np.zeros((0, 8), np.uint16), "bf16", "e4m3fn")
+    assert d.size == 0 and im.size == 0
