@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the MX quantize on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-calibration]
+
+A step is one full quantize of the workload tensor (one kernel launch: block
+scales, prescale, narrow, packing and scale placement). The input is
+generated on the device before timing and stays resident in HBM. The timed
+region is K back-to-back steps on one stream, bracketed by device
+synchronisation; every launch is also bracketed by its own pair of HIP events
+on that stream, which gives the kernel's average duration for the roofline.
+
+Prints one JSON line. ``value`` is algorithmic GB/s over the timed region:
+bytes per step = input (2 B/element) + data (1 B/element FP8, 0.5 B FP4) +
+logical scale (1/32 B/element); the never-written scale-image rows are not
+counted.
+
+``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
+write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
+WRITE_SIZE readings into bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MX quantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "bf16-131072x8192-colscaled"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
+                  "mx_microscaling_quantization_amd/csrc/mxq_api.hip"]
+
+
+def algorithmic_bytes(P: int, F: int, out: str) -> int:
+    n = P * F
+    data = n // 2 if out == "e2m1" else n
+    return 2 * n + data + n // 32
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, out: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "quantize_%s_%s_hbm_traffic.txt" % (workload, out))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def make_input(workload: str, device):
+    import numpy as np
+    import torch
+
+    import workloads
+
+    spec = workloads.WORKLOADS[workload]
+    P, F = spec["P"], spec["F"]
+    if workload == "bf16-131072x8192-colscaled":
+        xt = workloads.colscaled_bf16_device(P, F, seed=spec["seed"], device=str(device))
+    else:
+        x = workloads.make_host(workload)
+        tdt = torch.bfloat16 if spec["in_dtype"] == "bf16" else torch.float16
+        xt = torch.from_numpy(x.view(np.int16)).view(tdt).to(device)
+    return xt, spec
+
+
+def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows: int = 4096):
+    """The CPU oracle (single thread, as it stands) on leading row slabs of
+    the same input until about budget_s seconds of oracle time."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    oracle.build(force=False)
+    P, F = xt.shape
+    done_rows, spent = 0, 0.0
+    while done_rows < P and spent < budget_s:
+        rows = min(slab_rows, P - done_rows)
+        x = xt[done_rows:done_rows + rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.quantize(x, in_dtype, out)
+        spent += time.perf_counter() - t0
+        done_rows += rows
+    nbytes = algorithmic_bytes(done_rows, F, out)
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d rows (%d x %d, %.3g s of single-thread oracle time)"
+                      % (done_rows, P, done_rows, F, spent)}
+
+
+def copy_calibration(steps: int, warmup: int) -> None:
+    import torch
+
+    n = 1 << 30  # 2 GiB of bf16
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "ms_per_copy": round(ms, 4),
+                      "copy_GBps": round(4 * n / ms / 1e6, 1)}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--out", default=None, help="output format (default: the workload's first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this path runs on one GPU only; --gpus %d is not supported "
+              "(rows shard with no exchange, see the design notes)" % args.gpus, file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mx_microscaling_quantization_amd as mxq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration(args.steps, args.warmup)
+        return 0
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xt, spec = make_input(args.workload, dev)
+    out = args.out or spec["outs"][0]
+    P, F = xt.shape
+    data = torch.empty(mxq.data_shape(P, F, out), dtype=torch.uint8, device=dev)
+    image = torch.zeros(mxq.scale_image_shape(P, F), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for k in range(args.steps):
+        starts[k].record(stream)
+        mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+        ends[k].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    nbytes = algorithmic_bytes(P, F, out)
+    value = nbytes * args.steps / (total_ms * 1e-3) / 1e9
+    achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(args.workload, out)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec["in_dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "P": P, "F": F, "in": spec["in_dtype"], "out": out,
+                   "bytes_per_step": nbytes, "elements_per_step": P * F},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(P * F * args.steps / (total_ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel_avg_us": round(avg_launch_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"])
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

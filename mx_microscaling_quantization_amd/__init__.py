@@ -1,0 +1,150 @@
+"""MX (microscaling) quantize on AMD MI355X -- Python binding of ``libmxq.so``.
+
+A thin ctypes layer over the C ABI declared in ``include/mxq.h``: it maps
+torch dtypes to the ABI's codes, allocates outputs with torch when the caller
+gives none, and passes raw device pointers and the current HIP stream. Every
+step of the quantize runs in the library's HIP kernels; there is no fallback.
+If ``libmxq.so`` is missing or cannot be loaded, importing the functions below
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # loaded first so that the library binds to torch's HIP runtime
+
+__all__ = [
+    "IN_DTYPES", "OUT_DTYPES", "MXQError", "quantize", "data_bytes", "scale_image_bytes",
+    "data_shape", "scale_image_shape", "logical_scale_view", "status_string", "library_path", "load",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmxq.so"
+
+IN_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+OUT_DTYPES = {"e4m3fn": 0, "e5m2": 1, "e2m1": 2}
+ABI_VERSION = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MXQError(RuntimeError):
+    """A non-zero status from the library (``status`` holds the code)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("mxq status %d: %s" % (status, message))
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load():
+    """Load ``libmxq.so`` (once) and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError("%s is not built; run __graft_entry__.build() (hipcc, gfx950) first" % path)
+        lib = ctypes.CDLL(path)
+        c = ctypes
+        lib.mxq_quantize.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_void_p,
+                                     c.c_void_p, c.c_void_p]
+        lib.mxq_quantize.restype = c.c_int
+        lib.mxq_data_bytes.argtypes = [c.c_int64, c.c_int64, c.c_int]
+        lib.mxq_data_bytes.restype = c.c_size_t
+        lib.mxq_scale_image_bytes.argtypes = [c.c_int64, c.c_int64]
+        lib.mxq_scale_image_bytes.restype = c.c_size_t
+        lib.mxq_status_string.argtypes = [c.c_int]
+        lib.mxq_status_string.restype = c.c_char_p
+        lib.mxq_abi_version.argtypes = []
+        lib.mxq_abi_version.restype = c.c_int
+        if lib.mxq_abi_version() != ABI_VERSION:
+            raise ImportError("libmxq.so ABI %d, binding expects %d" % (lib.mxq_abi_version(), ABI_VERSION))
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().mxq_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MXQError(status, status_string(status))
+
+
+def _out_code(out_dtype: str) -> int:
+    try:
+        return OUT_DTYPES[out_dtype]
+    except KeyError:
+        raise MXQError(2, "output element type must be one of %s" % sorted(OUT_DTYPES)) from None
+
+
+def data_bytes(P: int, F: int, out_dtype: str) -> int:
+    return int(load().mxq_data_bytes(P, F, _out_code(out_dtype)))
+
+
+def scale_image_bytes(P: int, F: int) -> int:
+    return int(load().mxq_scale_image_bytes(P, F))
+
+
+def data_shape(P: int, F: int, out_dtype: str):
+    """uint8 shape of the data output: [P, F] (FP8) or [P, F/2] (FP4)."""
+    return (P, F // 2) if out_dtype == "e2m1" else (P, F)
+
+
+def scale_image_shape(P: int, F: int):
+    return (P, F // 4)
+
+
+def logical_scale_view(image: torch.Tensor) -> torch.Tensor:
+    """View [P/32, 4, F/4] of the written rows of a scale image (P % 32 == 0):
+    element [q, j, c] is the E8M0 of row group 4q + j, column block c."""
+    P, C = image.shape
+    if P % 32:
+        raise ValueError("logical_scale_view needs P % 32 == 0")
+    return image.view(P // 32, 32, C)[:, :4, :]
+
+
+def quantize(x: torch.Tensor, out_dtype: str = "e4m3fn", data_out: torch.Tensor | None = None,
+             scale_out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """MX-quantize a contiguous [P, F] bf16/f16 CUDA (HIP) tensor.
+
+    Returns ``(data, scale_image)`` as uint8 tensors: data [P, F] (FP8) or
+    [P, F/2] (FP4); the scale image [P, F/4], of which rows
+    (i mod 4) + 32 * floor(i / 4) hold row group i's E8M0 bytes and the other
+    rows keep whatever ``scale_out`` held. The kernel is enqueued on
+    ``stream`` (default: the current stream of x's device).
+    """
+    lib = load()
+    if x.dtype not in IN_DTYPES:
+        raise MXQError(1, "input element type must be bfloat16 or float16, got %s" % x.dtype)
+    code = _out_code(out_dtype)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [P, F]")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (row pitch F)")
+    P, F = x.shape
+    if data_out is None:
+        data_out = torch.empty(data_shape(P, F, out_dtype), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty(scale_image_shape(P, F), dtype=torch.uint8, device=x.device)
+    for name, t, nbytes in (("data_out", data_out, lib.mxq_data_bytes(P, F, code)),
+                            ("scale_out", scale_out, lib.mxq_scale_image_bytes(P, F))):
+        if t.device != x.device or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+            raise ValueError("%s must be a contiguous buffer of >= %d bytes on %s" % (name, nbytes, x.device))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.mxq_quantize(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, data_out.data_ptr(),
+                                scale_out.data_ptr(), stream.cuda_stream))
+    return data_out, scale_out

@@ -1,0 +1,133 @@
+// mxq_api.hip -- the C ABI of the MX quantize library (declared in mxq.h).
+//
+// Host side only: argument validation, launch geometry, dispatch on
+// (input type, output type, strip width) to the kernel templates, and the
+// launch itself on the caller's stream. No allocation, no state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxq.h"
+#include "mxq_quantize_kernels.hpp"
+
+namespace {
+
+// Threads per workgroup: four waves, or fewer when a row group has fewer
+// strips than that (rounded up to whole waves).
+constexpr uint32_t kMaxThreads = 256;
+
+// The kernel indexes strips, workgroups and per-row offsets with 32-bit
+// counts and 64-bit byte offsets; these bounds keep every count in range.
+constexpr int64_t kMaxF = (int64_t)1 << 31;
+constexpr int64_t kMaxWorkgroups = ((int64_t)1 << 31) - 1;
+
+typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t);
+
+template <int IN, int OUT> kernel_fn pick_nb(int nb)
+{
+    return nb == 2 ? (kernel_fn)mxq::quantize_kernel<IN, OUT, 2> : (kernel_fn)mxq::quantize_kernel<IN, OUT, 1>;
+}
+
+template <int IN> kernel_fn pick_out(int out_dtype, int nb)
+{
+    switch (out_dtype) {
+    case MXQ_OUT_E4M3FN: return pick_nb<IN, mxq::kOutE4M3FN>(nb);
+    case MXQ_OUT_E5M2: return pick_nb<IN, mxq::kOutE5M2>(nb);
+    default: return pick_nb<IN, mxq::kOutE2M1>(nb);
+    }
+}
+
+int check_shape(int64_t P, int64_t F)
+{
+    if (P < 0 || P % 8 != 0)
+        return MXQ_E_SHAPE_P8;
+    if (F < 0 || F % 4 != 0)
+        return MXQ_E_SHAPE_F4;
+    if (F > kMaxF)
+        return MXQ_E_OVERFLOW;
+    if (F > 0 && P > INT64_MAX / 2 / F)
+        return MXQ_E_OVERFLOW; // input bytes P*F*2 must fit
+    return MXQ_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+const char *mxq_status_string(int status)
+{
+    switch (status) {
+    case MXQ_OK: return "ok";
+    case MXQ_E_IN_DTYPE: return "input element type must be BF16 or F16";
+    case MXQ_E_OUT_DTYPE: return "output element type must be float8_e4m3fn, float8_e5m2 or float4_e2m1";
+    case MXQ_E_SHAPE_P8: return "P must be a non-negative multiple of 8 (a block spans 8 partitions)";
+    case MXQ_E_SHAPE_F4: return "F must be a non-negative multiple of 4 (x4 packing, 4 columns per block)";
+    case MXQ_E_NULL: return "a buffer pointer is NULL";
+    case MXQ_E_ALIGN: return "buffer pointers must be 16-byte aligned";
+    case MXQ_E_OVERFLOW: return "tensor too large for the library's index range";
+    case MXQ_E_HIP: return "the HIP runtime rejected the kernel launch";
+    case MXQ_E_FLAGS: return "unknown flag bits";
+    default: return "unknown status";
+    }
+}
+
+size_t mxq_data_bytes(int64_t P, int64_t F, int out_dtype)
+{
+    if (check_shape(P, F) != MXQ_OK)
+        return 0;
+    switch (out_dtype) {
+    case MXQ_OUT_E4M3FN:
+    case MXQ_OUT_E5M2: return (size_t)(P * F);
+    case MXQ_OUT_E2M1: return (size_t)(P * F / 2);
+    default: return 0;
+    }
+}
+
+size_t mxq_scale_image_bytes(int64_t P, int64_t F)
+{
+    if (check_shape(P, F) != MXQ_OK)
+        return 0;
+    return (size_t)(P * (F / 4));
+}
+
+int mxq_quantize(const void *in, int64_t P, int64_t F, int in_dtype, int out_dtype, void *data_out,
+                 void *scale_out, void *stream)
+{
+    if (in_dtype != MXQ_IN_BF16 && in_dtype != MXQ_IN_F16)
+        return MXQ_E_IN_DTYPE;
+    if (out_dtype != MXQ_OUT_E4M3FN && out_dtype != MXQ_OUT_E5M2 && out_dtype != MXQ_OUT_E2M1)
+        return MXQ_E_OUT_DTYPE;
+    int rc = check_shape(P, F);
+    if (rc != MXQ_OK)
+        return rc;
+    if (P == 0 || F == 0)
+        return MXQ_OK;
+    if (!in || !data_out || !scale_out)
+        return MXQ_E_NULL;
+    if (((uintptr_t)in | (uintptr_t)data_out | (uintptr_t)scale_out) & 15u)
+        return MXQ_E_ALIGN;
+
+    const int nb = (F % 8 == 0) ? 2 : 1;
+    const int64_t nstrips = F / (4 * nb);
+    const uint32_t threads = (uint32_t)(nstrips >= kMaxThreads ? kMaxThreads : ((nstrips + 63) / 64) * 64);
+    const int64_t tiles_per_group = (nstrips + threads - 1) / threads;
+    const int64_t groups = P / 8;
+    if (groups > kMaxWorkgroups / tiles_per_group)
+        return MXQ_E_OVERFLOW;
+
+    kernel_fn k = in_dtype == MXQ_IN_BF16 ? pick_out<mxq::kInBF16>(out_dtype, nb)
+                                          : pick_out<mxq::kInF16>(out_dtype, nb);
+    const uint16_t *a0 = (const uint16_t *)in;
+    uint8_t *a1 = (uint8_t *)data_out;
+    uint8_t *a2 = (uint8_t *)scale_out;
+    uint64_t a3 = (uint64_t)F;
+    uint32_t a4 = (uint32_t)nstrips;
+    uint32_t a5 = (uint32_t)tiles_per_group;
+    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5};
+    hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(groups * tiles_per_group)), dim3(threads),
+                                     args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
+}
+
+} // extern "C"

@@ -1,0 +1,269 @@
+// mxq_quantize_kernels.hpp -- gfx950 kernels of the MX quantize.
+//
+// One kernel pass per call: every byte of the input is read once from HBM,
+// every output byte is written once, nothing intermediate goes to memory.
+//
+// Work split. A thread owns a column strip of one row group: 8 rows x 4*NB
+// columns, i.e. NB whole 8x4 blocks (NB = 2 when F % 8 == 0, else 1). It
+// issues one 16-byte (NB = 2) or 8-byte (NB = 1) load per row, so a wave's
+// load of one row is 1 KiB (or 512 B) of contiguous memory. The block
+// maximum is then a reduction inside the thread's own registers -- no
+// cross-lane traffic, no LDS. A workgroup covers up to 256 consecutive
+// strips of one row group.
+//
+// Arithmetic ("MX Microscaling: Quantize, Block-Scaling and E8M0"):
+//  * the largest biased exponent of the fp32-widened block equals the
+//    exponent of the widened largest magnitude, because widening is
+//    monotone in |x|; so the kernel takes a packed 16-bit max over the
+//    magnitude bits (v_pk_max_u16) and widens only that one value
+//    (findMaxExponentPerInputBlock);
+//  * E8M0 = max(1, m - EMAX) (generateMxScales, both clamps at once);
+//  * prescale + round + pack run on gfx950's scaled conversions
+//    (v_cvt_scalef32_pk_{fp8,bf8,fp4}_{bf16,f16}), which compute
+//    RNE(x / scale) from the 16-bit inputs directly. With scale =
+//    2^(E8M0 - 127) that is exactly RNE(x * 2^(127 - E8M0))
+//    (quantizeDataApplyingMxScales followed by the narrow): the division by
+//    a power of two is exact and the product is rounded once, as in the
+//    page's fp32 multiply (whose own rounding only touches values far below
+//    every format's smallest subnormal);
+//  * these conversions do not saturate FP8/BF8: an overflow gives the NaN
+//    code (e4m3fn, 0x7F) or the Inf code (e5m2, 0x7C). A SWAR pass moves
+//    those bytes one code down, to the largest finite code;
+//  * NaN inputs: the conversions give a NaN code (FP8) or +-6 (FP4), while
+//    the quantizer's rule is a zero with the NaN's sign. A NaN can only sit
+//    in a block whose maximum magnitude pattern is above the Inf pattern, so
+//    a rarely taken per-thread branch rewrites exactly those codes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+enum { kInBF16 = 0, kInF16 = 1 };
+enum { kOutE4M3FN = 0, kOutE5M2 = 1, kOutE2M1 = 2 };
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// Largest normal exponent of each output format (the EMAX table).
+template <int OUT> struct Emax;
+template <> struct Emax<kOutE4M3FN> { static constexpr int value = 8; };
+template <> struct Emax<kOutE5M2> { static constexpr int value = 15; };
+template <> struct Emax<kOutE2M1> { static constexpr int value = 2; };
+
+// Magnitude pattern of +Inf in the input type; anything above it is a NaN.
+template <int IN> struct InfBits;
+template <> struct InfBits<kInBF16> { static constexpr uint32_t value = 0x7F80u; };
+template <> struct InfBits<kInF16> { static constexpr uint32_t value = 0x7C00u; };
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
+{
+    u16x2_t x = __builtin_bit_cast(u16x2_t, a);
+    u16x2_t y = __builtin_bit_cast(u16x2_t, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// Biased fp32 exponent field of the widened value whose 16-bit magnitude
+// pattern is `mag` (sign already cleared).
+template <int IN> __device__ __forceinline__ uint32_t widened_exponent(uint32_t mag)
+{
+    if constexpr (IN == kInBF16) {
+        return mag >> 7; // bf16 keeps the fp32 exponent field in bits 14..7
+    } else {
+        // exact f16 -> f32 (f16 subnormals become fp32 normals)
+        float f = (float)__builtin_bit_cast(_Float16, (uint16_t)mag);
+        return (__float_as_uint(f) >> 23) & 0xFFu;
+    }
+}
+
+// E8M0 of one block given the magnitude max over its 32 elements.
+template <int IN, int OUT> __device__ __forceinline__ uint32_t block_e8m0(uint32_t mag)
+{
+    int v = (int)widened_exponent<IN>(mag) - Emax<OUT>::value;
+    return (uint32_t)(v < 1 ? 1 : v);
+}
+
+// The conversion's scale operand for an E8M0 byte: the fp32 2^(e - 127).
+__device__ __forceinline__ float e8m0_to_scale(uint32_t e) { return __uint_as_float(e << 23); }
+
+// Four FP8 codes (one u32 lane) from two input dwords holding elements
+// (0,1) and (2,3), saturated.
+template <int IN, int OUT> __device__ __forceinline__ uint32_t fp8x4(uint32_t p01, uint32_t p23, float s)
+{
+    i16x2_t r = {0, 0};
+    if constexpr (IN == kInBF16) {
+        bf16x2_t a = __builtin_bit_cast(bf16x2_t, p01), b = __builtin_bit_cast(bf16x2_t, p23);
+        if constexpr (OUT == kOutE4M3FN) {
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, a, s, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, b, s, true);
+        } else {
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, a, s, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, b, s, true);
+        }
+    } else {
+        f16x2_t a = __builtin_bit_cast(f16x2_t, p01), b = __builtin_bit_cast(f16x2_t, p23);
+        if constexpr (OUT == kOutE4M3FN) {
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, a, s, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, b, s, true);
+        } else {
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f16(r, a, s, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f16(r, b, s, true);
+        }
+    }
+    uint32_t w = __builtin_bit_cast(uint32_t, r);
+    // Overflow codes: e4m3fn 0x7F (NaN) and e5m2 0x7C (Inf), either sign.
+    // Adding 1 (resp. 4) to the low 7 bits of a byte carries into bit 7 for
+    // exactly those codes (and e5m2's NaN codes, which only a NaN input makes
+    // and the NaN pass rewrites); subtracting that carry gives 0x7E / 0x7B.
+    constexpr uint32_t bump = OUT == kOutE4M3FN ? 0x01010101u : 0x04040404u;
+    uint32_t t = ((w & 0x7F7F7F7Fu) + bump) & 0x80808080u;
+    return w - (t >> 7);
+}
+
+// One FP4 container (16 bits) from elements (0,1) in p01 and (2,3) in p23,
+// placed as byte 0 = e2 | e3 << 4, byte 1 = e0 | e1 << 4, and written into
+// bytes 2*HALF, 2*HALF+1 of `acc`.
+template <int IN, int HALF>
+__device__ __forceinline__ uint32_t fp4_container(uint32_t acc, uint32_t p01, uint32_t p23, float s)
+{
+    if constexpr (IN == kInBF16) {
+        bf16x2_t a = __builtin_bit_cast(bf16x2_t, p01), b = __builtin_bit_cast(bf16x2_t, p23);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, b, s, 2 * HALF);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, a, s, 2 * HALF + 1);
+    } else {
+        f16x2_t a = __builtin_bit_cast(f16x2_t, p01), b = __builtin_bit_cast(f16x2_t, p23);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(acc, b, s, 2 * HALF);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(acc, a, s, 2 * HALF + 1);
+    }
+    return acc;
+}
+
+// Bit offset, inside the u32 holding a row's FP4 output for one strip, of
+// element k (0..7) of the strip: container k/4, then {8, 12, 0, 4}.
+__device__ __forceinline__ uint32_t fp4_bit_offset(uint32_t k)
+{
+    return 16u * (k >> 2) + ((0x40C8u >> (4u * (k & 3u))) & 0xFu);
+}
+
+// Rewrite the codes of NaN elements to a zero of the NaN's sign. `w` holds
+// the input dwords of one row (2*NB of them), `out` the row's output codes:
+// FP8 in out[0..NB-1] (byte k of the strip = element k), FP4 in out[0].
+template <int IN, int OUT, int NB>
+__device__ __forceinline__ void nan_to_signed_zero(const uint32_t *w, uint32_t *out)
+{
+#pragma unroll
+    for (uint32_t k = 0; k < 4 * NB; k++) {
+        uint32_t h = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+        if ((h & 0x7FFFu) <= InfBits<IN>::value)
+            continue;
+        uint32_t sign = h >> 15;
+        if constexpr (OUT == kOutE2M1) {
+            uint32_t sh = fp4_bit_offset(k);
+            out[0] = (out[0] & ~(0xFu << sh)) | ((sign << 3) << sh);
+        } else {
+            uint32_t sh = 8 * (k & 3);
+            out[k >> 2] = (out[k >> 2] & ~(0xFFu << sh)) | ((sign << 7) << sh);
+        }
+    }
+}
+
+template <int NB> struct Vec;
+template <> struct Vec<2> { typedef uint4 type; };
+template <> struct Vec<1> { typedef uint2 type; };
+
+__device__ __forceinline__ void unpack(const uint4 &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; }
+__device__ __forceinline__ void unpack(const uint2 &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; }
+
+// The quantize kernel. Grid: one workgroup per (row group, run of up to
+// blockDim.x strips); `tiles_per_group` runs per row group.
+//   F          columns (pitch of the input and of FP8 data), F % (4*NB) == 0
+//   nstrips    F / (4*NB)
+template <int IN, int OUT, int NB>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ in,
+                                                       uint8_t *__restrict__ data,
+                                                       uint8_t *__restrict__ scale,
+                                                       uint64_t F, uint32_t nstrips,
+                                                       uint32_t tiles_per_group)
+{
+    typedef typename Vec<NB>::type vec_t;
+    const uint32_t group = blockIdx.x / tiles_per_group;
+    const uint32_t strip = (blockIdx.x - group * tiles_per_group) * blockDim.x + threadIdx.x;
+    if (strip >= nstrips)
+        return;
+
+    const uint64_t row0 = (uint64_t)group * 8u;
+    const uint64_t pitch = F / (4 * NB); // row pitch in vec_t units
+    const vec_t *src = reinterpret_cast<const vec_t *>(in + row0 * F) + strip;
+
+    uint32_t w[8][2 * NB];
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+        unpack(src[r * pitch], w[r]);
+
+    // Block maxima of the magnitude patterns, two 16-bit lanes at a time.
+    uint32_t mag[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            m = pk_max_u16(m, w[r][2 * b] & 0x7FFF7FFFu);
+            m = pk_max_u16(m, w[r][2 * b + 1] & 0x7FFF7FFFu);
+        }
+        mag[b] = max(m & 0xFFFFu, m >> 16);
+    }
+
+    uint32_t e[NB];
+    float s[NB];
+    bool has_nan = false;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        e[b] = block_e8m0<IN, OUT>(mag[b]);
+        s[b] = e8m0_to_scale(e[b]);
+        has_nan |= mag[b] > InfBits<IN>::value;
+    }
+
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        const uint64_t row = row0 + r;
+        if constexpr (OUT == kOutE2M1) {
+            uint32_t out[1] = {0};
+            out[0] = fp4_container<IN, 0>(out[0], w[r][0], w[r][1], s[0]);
+            if constexpr (NB == 2)
+                out[0] = fp4_container<IN, 1>(out[0], w[r][2], w[r][3], s[1]);
+            if (has_nan)
+                nan_to_signed_zero<IN, OUT, NB>(w[r], out);
+            uint8_t *dst = data + (row * F) / 2 + (uint64_t)strip * (2 * NB);
+            if constexpr (NB == 2)
+                *reinterpret_cast<uint32_t *>(dst) = out[0];
+            else
+                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)out[0];
+        } else {
+            uint32_t out[NB];
+#pragma unroll
+            for (int b = 0; b < NB; b++)
+                out[b] = fp8x4<IN, OUT>(w[r][2 * b], w[r][2 * b + 1], s[b]);
+            if (has_nan)
+                nan_to_signed_zero<IN, OUT, NB>(w[r], out);
+            uint8_t *dst = data + row * F + (uint64_t)strip * (4 * NB);
+            if constexpr (NB == 2)
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
+            else
+                *reinterpret_cast<uint32_t *>(dst) = out[0];
+        }
+    }
+
+    // Scale placement: logical row `group` goes to image row
+    // (group mod 4) + 32 * floor(group / 4).
+    const uint64_t slot = (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
+    uint8_t *sdst = scale + slot * (F / 4) + (uint64_t)strip * NB;
+    if constexpr (NB == 2)
+        *reinterpret_cast<uint16_t *>(sdst) = (uint16_t)(e[0] | (e[1] << 8));
+    else
+        *sdst = (uint8_t)e[0];
+}
+
+} // namespace mxq

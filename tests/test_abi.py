@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function ``include/mxq.h`` declares, agree
+with the header's enum values, and reject bad arguments before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mx_microscaling_quantization_amd as mxq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def _header_text():
+    with open(HEADER) as fh:
+        return fh.read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
+
+
+def _header_enums():
+    vals = {}
+    for name, val in re.findall(r"\b(MXQ_[A-Z0-9_]+)\s*=\s*(\d+)", _header_text()):
+        vals[name] = int(val)
+    return vals
+
+
+def test_library_exports_every_declared_function():
+    lib = mxq.load()
+    names = _declared_functions()
+    assert {"mxq_quantize", "mxq_data_bytes", "mxq_scale_image_bytes", "mxq_status_string",
+            "mxq_abi_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the shared object's dynamic symbol table has them as functions
+    out = os.popen("nm -D --defined-only %s" % mxq.library_path()).read()
+    for name in names:
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_enum_values_agree_with_binding():
+    e = _header_enums()
+    assert e["MXQ_IN_BF16"] == 0 and e["MXQ_IN_F16"] == 1
+    assert {k: e["MXQ_OUT_" + k.upper()] for k in mxq.OUT_DTYPES} == mxq.OUT_DTYPES
+    lib = mxq.load()
+    assert lib.mxq_abi_version() == int(re.search(r"MXQ_ABI_VERSION (\d+)", _header_text()).group(1))
+
+
+def test_status_strings():
+    e = _header_enums()
+    codes = [v for k, v in e.items() if k.startswith("MXQ_E_") or k == "MXQ_OK"]
+    msgs = {mxq.status_string(c) for c in codes}
+    assert len(msgs) == len(codes)
+    assert mxq.status_string(12345) == "unknown status"
+    assert "multiple of 8" in mxq.status_string(e["MXQ_E_SHAPE_P8"])
+    assert "divisible" in mxq.status_string(e["MXQ_E_SHAPE_F4"]) or "multiple of 4" in mxq.status_string(
+        e["MXQ_E_SHAPE_F4"])
+
+
+@pytest.mark.parametrize("P,F,out,expect", [
+    (16, 8, "e4m3fn", 128), (16, 8, "e5m2", 128), (16, 8, "e2m1", 64),
+    (0, 8, "e4m3fn", 0), (8, 0, "e2m1", 0), (131072, 8192, "e4m3fn", 131072 * 8192),
+    (12, 8, "e4m3fn", 0), (8, 6, "e4m3fn", 0), (-8, 4, "e4m3fn", 0),
+])
+def test_data_bytes(P, F, out, expect):
+    assert mxq.data_bytes(P, F, out) == expect
+
+
+def test_scale_image_bytes():
+    assert mxq.scale_image_bytes(16, 8) == 32
+    assert mxq.scale_image_bytes(131072, 8192) == 131072 * 2048
+    assert mxq.scale_image_bytes(12, 8) == 0
+    lib = mxq.load()
+    assert lib.mxq_data_bytes(16, 8, 7) == 0
+
+
+def _call(in_ptr, P, F, in_dtype, out_dtype, d, s):
+    return mxq.load().mxq_quantize(in_ptr, P, F, in_dtype, out_dtype, d, s, None)
+
+
+def test_validation_errors_before_launch():
+    e = _header_enums()
+    good = 4096  # a 16-byte aligned fake address: never dereferenced, calls fail validation first
+    assert _call(good, 16, 8, 2, 0, good, good) == e["MXQ_E_IN_DTYPE"]
+    assert _call(good, 16, 8, -1, 0, good, good) == e["MXQ_E_IN_DTYPE"]
+    assert _call(good, 16, 8, 0, 3, good, good) == e["MXQ_E_OUT_DTYPE"]
+    assert _call(good, 12, 8, 0, 0, good, good) == e["MXQ_E_SHAPE_P8"]
+    assert _call(good, -8, 8, 0, 0, good, good) == e["MXQ_E_SHAPE_P8"]
+    assert _call(good, 16, 6, 0, 0, good, good) == e["MXQ_E_SHAPE_F4"]
+    assert _call(good, 16, -4, 0, 0, good, good) == e["MXQ_E_SHAPE_F4"]
+    assert _call(good, 1 << 40, 1 << 30, 0, 0, good, good) == e["MXQ_E_OVERFLOW"]
+    assert _call(good, 8, (1 << 31) + 4, 0, 0, good, good) == e["MXQ_E_OVERFLOW"]
+    assert _call(None, 16, 8, 0, 0, good, good) == e["MXQ_E_NULL"]
+    assert _call(good, 16, 8, 0, 0, None, good) == e["MXQ_E_NULL"]
+    assert _call(good, 16, 8, 0, 0, good, None) == e["MXQ_E_NULL"]
+    assert _call(good + 8, 16, 8, 0, 0, good, good) == e["MXQ_E_ALIGN"]
+    assert _call(good, 16, 8, 1, 2, good + 2, good) == e["MXQ_E_ALIGN"]
+    assert _call(good, 16, 8, 1, 1, good, good + 1) == e["MXQ_E_ALIGN"]
+
+
+def test_empty_tensors_are_noops():
+    for P, F in ((0, 8), (8, 0), (0, 0)):
+        for out in range(3):
+            assert _call(None, P, F, 0, out, None, None) == 0
+
+
+def test_binding_rejects_before_calling():
+    import torch
+
+    with pytest.raises(mxq.MXQError):
+        mxq.quantize(torch.zeros(8, 8, dtype=torch.float32), "e4m3fn")
+    with pytest.raises(mxq.MXQError):
+        mxq.quantize(torch.zeros(8, 8, dtype=torch.bfloat16), "int8")
+    with pytest.raises(ValueError):
+        mxq.quantize(torch.zeros(8, 8, dtype=torch.bfloat16), "e4m3fn")   # not a device tensor
+
+
+def test_library_does_not_link_the_oracle():
+    out = os.popen("nm -D %s" % mxq.library_path()).read()
+    assert "oracle" not in out
+    deps = os.popen("readelf -d %s" % mxq.library_path()).read()
+    assert "oracle" not in deps

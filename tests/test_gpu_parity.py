@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact on both outputs (quantized codes are integer results). Every case
+also checks that the scale image rows the placement does not name keep their
+sentinel and that nothing is written past the end of the data buffer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_microscaling_quantization_amd as mxq
+import oracle
+import workloads
+from conftest import progress
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16}
+EMAX = {"e2m1": 2, "e4m3fn": 8, "e5m2": 15}
+COMBOS = [(i, o) for i in ("bf16", "f16") for o in ("e4m3fn", "e5m2", "e2m1")]
+SENTINEL = 0xA5
+GUARD = 256
+
+
+def to_device(x: np.ndarray, in_dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(TDT[in_dtype]).to("cuda")
+
+
+def gpu_quantize(xt: torch.Tensor, out: str, stream=None):
+    """Quantize through the binding into guarded, sentinel-filled buffers.
+    Returns numpy (data, image) after checking the guard band."""
+    P, F = xt.shape
+    nbytes = mxq.data_bytes(P, F, out)
+    buf = torch.full((nbytes + GUARD,), 0xEE, dtype=torch.uint8, device=xt.device)
+    data = buf[:nbytes].view(mxq.data_shape(P, F, out))
+    image = torch.full(mxq.scale_image_shape(P, F), SENTINEL, dtype=torch.uint8, device=xt.device)
+    mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+    torch.cuda.synchronize()
+    tail = buf[nbytes:].cpu().numpy()
+    assert np.all(tail == 0xEE), "write past the end of the data buffer"
+    return data.cpu().numpy(), image.cpu().numpy()
+
+
+def check_against_oracle(x: np.ndarray, in_dtype: str, out: str, tag: str):
+    progress("%s %s->%s shape=%s" % (tag, in_dtype, out, x.shape))
+    d_gpu, im_gpu = gpu_quantize(to_device(x, in_dtype), out)
+    fill = np.full((x.shape[0], x.shape[1] // 4), SENTINEL, np.uint8)
+    d_ref, im_ref = oracle.quantize(x, in_dtype, out, image=fill)
+    if not np.array_equal(d_gpu, d_ref):
+        bad = np.argwhere(d_gpu != d_ref)
+        r, c = bad[0]
+        raise AssertionError("%s: %d data bytes differ, first at %s: gpu %#x oracle %#x"
+                             % (tag, len(bad), (r, c), d_gpu[r, c], d_ref[r, c]))
+    if not np.array_equal(im_gpu, im_ref):
+        bad = np.argwhere(im_gpu != im_ref)
+        r, c = bad[0]
+        raise AssertionError("%s: %d scale bytes differ, first at %s: gpu %#x oracle %#x"
+                             % (tag, len(bad), (r, c), im_gpu[r, c], im_ref[r, c]))
+
+
+# ---------------------------------------------------------------- small shapes
+
+SHAPES = [(8, 4), (8, 8), (16, 12), (40, 8), (40, 12), (64, 96), (8, 2056), (264, 1032),
+          (136, 2052), (256, 4100), (32, 8192), (1032, 520)]
+
+
+@pytest.mark.parametrize("in_dtype,out", COMBOS)
+@pytest.mark.parametrize("P,F", SHAPES)
+def test_shapes_with_specials(in_dtype, out, P, F):
+    x = workloads.random_bits(P, F, in_dtype, seed=P * 7919 + F, specials=True)
+    check_against_oracle(x, in_dtype, out, "shape")
+
+
+@pytest.mark.parametrize("in_dtype,out", COMBOS)
+def test_nonfinite_blocks(in_dtype, out):
+    P, F = 32, 64
+    x = workloads.random_bits(P, F, in_dtype, seed=5)
+    inf = 0x7F80 if in_dtype == "bf16" else 0x7C00
+    nan = 0x7FC0 if in_dtype == "bf16" else 0x7E00
+    b = x.reshape(P // 8, 8, F // 4, 4)
+    b[0, 0, 0, 0] = inf                  # +Inf with finite neighbours
+    b[0, 1, 1, 2] = inf | 0x8000         # -Inf
+    b[1, 3, 2, 1] = nan                  # NaN
+    b[1, 4, 3, 0] = nan | 0x8000         # -NaN
+    b[2, :, 4, :] = nan                  # all NaN
+    b[2, :, 5, :] = inf | 0x8000         # all -Inf
+    b[3, 0, 6, 0] = nan
+    b[3, 0, 6, 1] = inf                  # NaN and Inf together
+    check_against_oracle(x, in_dtype, out, "nonfinite")
+
+
+def _pilot_sweep(in_dtype: str) -> np.ndarray:
+    """Blocks that put every input pattern under every scale it can meet:
+    for each reachable block maximum exponent m, one pilot element with
+    exponent m and every pattern whose exponent is at most m, 31 per block."""
+    h = np.arange(65536, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        f32 = workloads.bf16_bits_to_f32(h) if in_dtype == "bf16" else h.view(np.float16).astype(np.float32)
+    ex = (f32.view(np.uint32) >> 23) & 0xFF
+    blocks = []
+    for m in np.unique(ex):
+        pilot = h[(ex == m) & (h < 0x8000)][0]
+        cand = h[ex <= m]
+        pad = (-cand.size) % 31
+        cand = np.concatenate([cand, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        blocks.append(np.concatenate([np.full((cand.shape[0], 1), pilot, np.uint16), cand], axis=1))
+    blocks = np.concatenate(blocks)
+    ncb = 256
+    nrg = -(-blocks.shape[0] // ncb)
+    blocks = np.concatenate([blocks, np.zeros((nrg * ncb - blocks.shape[0], 32), np.uint16)])
+    # block b -> row group b // ncb, column block b % ncb; element k -> (k // 4, k % 4)
+    return blocks.reshape(nrg, ncb, 8, 4).transpose(0, 2, 1, 3).reshape(nrg * 8, ncb * 4)
+
+
+@pytest.mark.parametrize("in_dtype,out", COMBOS)
+def test_exhaustive_pattern_scale_sweep(in_dtype, out):
+    x = _pilot_sweep(in_dtype)
+    check_against_oracle(x, in_dtype, out, "sweep")
+
+
+# ------------------------------------------------------------------ workloads
+
+def test_workload_bf16_128x512_handplaced():
+    check_against_oracle(workloads.handplaced_bf16_128x512(), "bf16", "e4m3fn", "bf16-128x512-handplaced")
+
+
+@pytest.mark.parametrize("out", ["e4m3fn", "e5m2"])
+def test_workload_bf16_4096x4096_rowscaled(out):
+    check_against_oracle(workloads.rowscaled_bf16(), "bf16", out, "bf16-4096x4096-rowscaled")
+
+
+def test_workload_f16_8192x14336_student_t():
+    check_against_oracle(workloads.student_t_f16(), "f16", "e5m2", "f16-8192x14336-student-t")
+
+
+def test_workload_bf16_16384x8192_blockexp():
+    check_against_oracle(workloads.blockexp_bf16(), "bf16", "e2m1", "bf16-16384x8192-blockexp")
+
+
+def test_workload_bf16_131072x8192_colscaled_sampled():
+    """Full size, same call as the bench; the oracle checks 48 sampled 32-row
+    slabs (every column), and properties are checked everywhere."""
+    P, F = 131072, 8192
+    progress("bf16-131072x8192-colscaled: generate on device")
+    xt = workloads.colscaled_bf16_device(P, F, seed=5)
+    progress("bf16-131072x8192-colscaled: quantize")
+    data = torch.empty((P, F), dtype=torch.uint8, device="cuda")
+    image = torch.full((P, F // 4), SENTINEL, dtype=torch.uint8, device="cuda")
+    mxq.quantize(xt, "e4m3fn", data_out=data, scale_out=image)
+    torch.cuda.synchronize()
+    progress("bf16-131072x8192-colscaled: sampled oracle check")
+    rng = np.random.default_rng(55)
+    slabs = np.unique(np.concatenate([[0, P // 32 - 1], rng.integers(0, P // 32, size=46)]))
+    for q in slabs:
+        rows = slice(32 * int(q), 32 * int(q) + 32)
+        x = xt[rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        fill = np.full((32, F // 4), SENTINEL, np.uint8)
+        d_ref, im_ref = oracle.quantize(x, "bf16", "e4m3fn", image=fill)
+        assert np.array_equal(data[rows].cpu().numpy(), d_ref), "slab %d data" % q
+        assert np.array_equal(image[rows].cpu().numpy(), im_ref), "slab %d scale image" % q
+    progress("bf16-131072x8192-colscaled: whole-tensor properties")
+    # finite input: no NaN codes anywhere; every placed scale in range; every
+    # unplaced image row untouched
+    assert not bool(((data & 0x7F) == 0x7F).any())
+    img = image.view(P // 32, 32, F // 4)
+    placed = img[:, :4, :]
+    assert int(placed.min()) >= 1 and int(placed.max()) <= 254 - 8
+    assert bool((img[:, 4:, :] == SENTINEL).all())
+
+
+# --------------------------------------------------------------- other checks
+
+def test_deterministic_across_runs_and_streams():
+    x = workloads.random_bits(1024, 4096, "bf16", seed=9, specials=True)
+    xt = to_device(x, "bf16")
+    ref = gpu_quantize(xt, "e4m3fn")
+    s = torch.cuda.Stream()
+    for k in range(5):
+        got = gpu_quantize(xt, "e4m3fn", stream=s if k % 2 else None)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_empty_and_misaligned_on_device():
+    for shape in ((0, 8), (8, 0)):
+        xt = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        d, im = mxq.quantize(xt, "e4m3fn")
+        assert d.numel() == 0 or im.numel() == 0
+    flat = torch.zeros(8 * 8 + 1, dtype=torch.bfloat16, device="cuda")
+    xt = flat[1:].view(8, 8)
+    with pytest.raises(mxq.MXQError) as ei:
+        mxq.quantize(xt, "e4m3fn")
+    assert ei.value.status == 6
+
+
+def test_outputs_on_caller_stream():
+    """The kernel is enqueued on the given stream: work queued behind a
+    long-running op on that stream sees the op's result."""
+    x = workloads.random_bits(512, 2048, "f16", seed=10)
+    xt = to_device(x, "f16")
+    s = torch.cuda.Stream()
+    src = torch.zeros_like(xt)
+    with torch.cuda.stream(s):
+        src.copy_(xt)        # queued on s before the quantize
+        d, im = mxq.quantize(src, "e5m2")
+    s.synchronize()
+    d_ref, _ = oracle.quantize(x, "f16", "e5m2")
+    assert np.array_equal(d.cpu().numpy(), d_ref)
