@@ -51,7 +51,7 @@ def load():
             return _lib
         path = library_path()
         if not os.path.exists(path):
-            raise ImportError("%s is not built; run __graft_entry__.build() (hipcc, gfx950) first" % path)
+            raise ImportError("%s is not built; run `python -m mx_microscaling_quantization_amd._build` (hipcc, gfx950) first" % path)
         lib = ctypes.CDLL(path)
         c = ctypes
         lib.mxq_quantize.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_void_p,

@@ -8,8 +8,9 @@
 // issues one 16-byte (NB = 2) or 8-byte (NB = 1) load per row, so a wave's
 // load of one row is 1 KiB (or 512 B) of contiguous memory. The block
 // maximum is then a reduction inside the thread's own registers -- no
-// cross-lane traffic, no LDS. A workgroup covers up to 256 consecutive
-// strips of one row group.
+// cross-lane traffic, no LDS. A workgroup (one wave) covers 64 consecutive
+// strips of one row group. Loads and stores carry the non-temporal hint:
+// the data streams through once.
 //
 // Arithmetic ("MX Microscaling: Quantize, Block-Scaling and E8M0"):
 //  * the largest biased exponent of the fp32-widened block equals the
@@ -170,100 +171,152 @@ __device__ __forceinline__ void nan_to_signed_zero(const uint32_t *w, uint32_t *
     }
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 template <int NB> struct Vec;
-template <> struct Vec<2> { typedef uint4 type; };
-template <> struct Vec<1> { typedef uint2 type; };
+template <> struct Vec<2> { typedef u32x4_t type; };
+template <> struct Vec<1> { typedef u32x2_t type; };
 
-__device__ __forceinline__ void unpack(const uint4 &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; }
-__device__ __forceinline__ void unpack(const uint2 &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; }
+__device__ __forceinline__ void unpack(const u32x4_t &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; }
+__device__ __forceinline__ void unpack(const u32x2_t &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; }
 
-// The quantize kernel. Grid: one workgroup per (row group, run of up to
-// blockDim.x strips); `tiles_per_group` runs per row group.
+// Loads and stores with an optional non-temporal hint (streaming data that
+// no later access of this kernel touches again).
+template <int NT, typename T> __device__ __forceinline__ T load(const T *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+template <int NT, typename T> __device__ __forceinline__ void store(T *p, T v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+// The quantize kernel.
+//
+// Grid: one workgroup per (band, run of up to blockDim.x strips), where a
+// band is GPT consecutive row groups and `tiles_per_band` runs cover a band.
+// Each thread quantizes the same strip in every row group of its band; all
+// 8*GPT row loads are issued before any arithmetic. NT bit 0 marks the loads
+// non-temporal, bit 1 the stores. XCD != 0 renumbers workgroups so that each
+// of the XCD chiplets (which receive workgroups round-robin) walks one
+// contiguous range of tiles.
 //   F          columns (pitch of the input and of FP8 data), F % (4*NB) == 0
 //   nstrips    F / (4*NB)
-template <int IN, int OUT, int NB>
+//   ngroups    P / 8
+template <int XCD> __device__ __forceinline__ uint32_t tile_index()
+{
+    if constexpr (XCD == 0) {
+        return blockIdx.x;
+    } else {
+        // workgroup i runs on chiplet i mod XCD; give chiplet c the tiles
+        // [c*q, (c+1)*q) of the first XCD*q, and leave the tail in place
+        const uint32_t q = gridDim.x / XCD;
+        const uint32_t i = blockIdx.x;
+        return i < q * XCD ? (i % XCD) * q + i / XCD : i;
+    }
+}
+
+template <int IN, int OUT, int NB, int GPT, int NT, int XCD = 0>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ in,
                                                        uint8_t *__restrict__ data,
                                                        uint8_t *__restrict__ scale,
                                                        uint64_t F, uint32_t nstrips,
-                                                       uint32_t tiles_per_group)
+                                                       uint32_t tiles_per_band, uint32_t ngroups)
 {
     typedef typename Vec<NB>::type vec_t;
-    const uint32_t group = blockIdx.x / tiles_per_group;
-    const uint32_t strip = (blockIdx.x - group * tiles_per_group) * blockDim.x + threadIdx.x;
+    const uint32_t tile = tile_index<XCD>();
+    const uint32_t band = tile / tiles_per_band;
+    const uint32_t strip = (tile - band * tiles_per_band) * blockDim.x + threadIdx.x;
     if (strip >= nstrips)
         return;
 
-    const uint64_t row0 = (uint64_t)group * 8u;
     const uint64_t pitch = F / (4 * NB); // row pitch in vec_t units
-    const vec_t *src = reinterpret_cast<const vec_t *>(in + row0 * F) + strip;
+    const uint32_t g0 = band * GPT;
 
-    uint32_t w[8][2 * NB];
+    uint32_t w[GPT][8][2 * NB];
 #pragma unroll
-    for (int r = 0; r < 8; r++)
-        unpack(src[r * pitch], w[r]);
+    for (int j = 0; j < GPT; j++) {
+        if (GPT > 1 && g0 + j >= ngroups)
+            break;
+        const vec_t *src = reinterpret_cast<const vec_t *>(in + (uint64_t)(g0 + j) * 8u * F) + strip;
+#pragma unroll
+        for (int r = 0; r < 8; r++)
+            unpack(load<NT & 1>(src + r * pitch), w[j][r]);
+    }
 
-    // Block maxima of the magnitude patterns, two 16-bit lanes at a time.
-    uint32_t mag[NB];
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-        uint32_t m = 0;
+    for (int j = 0; j < GPT; j++) {
+        const uint32_t group = g0 + j;
+        if (GPT > 1 && group >= ngroups)
+            break;
+        const uint64_t row0 = (uint64_t)group * 8u;
+
+        // Block maxima of the magnitude patterns, two 16-bit lanes at a time.
+        uint32_t e[NB];
+        float s[NB];
+        bool has_nan = false;
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                m = pk_max_u16(m, w[j][r][2 * b] & 0x7FFF7FFFu);
+                m = pk_max_u16(m, w[j][r][2 * b + 1] & 0x7FFF7FFFu);
+            }
+            const uint32_t mag = max(m & 0xFFFFu, m >> 16);
+            e[b] = block_e8m0<IN, OUT>(mag);
+            s[b] = e8m0_to_scale(e[b]);
+            has_nan |= mag > InfBits<IN>::value;
+        }
+
 #pragma unroll
         for (int r = 0; r < 8; r++) {
-            m = pk_max_u16(m, w[r][2 * b] & 0x7FFF7FFFu);
-            m = pk_max_u16(m, w[r][2 * b + 1] & 0x7FFF7FFFu);
+            const uint64_t row = row0 + r;
+            if constexpr (OUT == kOutE2M1) {
+                uint32_t out[1] = {0};
+                out[0] = fp4_container<IN, 0>(out[0], w[j][r][0], w[j][r][1], s[0]);
+                if constexpr (NB == 2)
+                    out[0] = fp4_container<IN, 1>(out[0], w[j][r][2], w[j][r][3], s[1]);
+                if (has_nan)
+                    nan_to_signed_zero<IN, OUT, NB>(w[j][r], out);
+                uint8_t *dst = data + (row * F) / 2 + (uint64_t)strip * (2 * NB);
+                if constexpr (NB == 2)
+                    store<(NT >> 1) & 1>(reinterpret_cast<uint32_t *>(dst), out[0]);
+                else
+                    store<(NT >> 1) & 1>(reinterpret_cast<uint16_t *>(dst), (uint16_t)out[0]);
+            } else {
+                uint32_t out[NB];
+#pragma unroll
+                for (int b = 0; b < NB; b++)
+                    out[b] = fp8x4<IN, OUT>(w[j][r][2 * b], w[j][r][2 * b + 1], s[b]);
+                if (has_nan)
+                    nan_to_signed_zero<IN, OUT, NB>(w[j][r], out);
+                uint8_t *dst = data + row * F + (uint64_t)strip * (4 * NB);
+                if constexpr (NB == 2) {
+                    u32x2_t v = {out[0], out[1]};
+                    store<(NT >> 1) & 1>(reinterpret_cast<u32x2_t *>(dst), v);
+                } else {
+                    store<(NT >> 1) & 1>(reinterpret_cast<uint32_t *>(dst), out[0]);
+                }
+            }
         }
-        mag[b] = max(m & 0xFFFFu, m >> 16);
-    }
 
-    uint32_t e[NB];
-    float s[NB];
-    bool has_nan = false;
-#pragma unroll
-    for (int b = 0; b < NB; b++) {
-        e[b] = block_e8m0<IN, OUT>(mag[b]);
-        s[b] = e8m0_to_scale(e[b]);
-        has_nan |= mag[b] > InfBits<IN>::value;
+        // Scale placement: logical row `group` goes to image row
+        // (group mod 4) + 32 * floor(group / 4).
+        const uint64_t slot = (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
+        uint8_t *sdst = scale + slot * (F / 4) + (uint64_t)strip * NB;
+        if constexpr (NB == 2)
+            store<(NT >> 1) & 1>(reinterpret_cast<uint16_t *>(sdst), (uint16_t)(e[0] | (e[1] << 8)));
+        else
+            store<(NT >> 1) & 1>(sdst, (uint8_t)e[0]);
     }
-
-#pragma unroll
-    for (int r = 0; r < 8; r++) {
-        const uint64_t row = row0 + r;
-        if constexpr (OUT == kOutE2M1) {
-            uint32_t out[1] = {0};
-            out[0] = fp4_container<IN, 0>(out[0], w[r][0], w[r][1], s[0]);
-            if constexpr (NB == 2)
-                out[0] = fp4_container<IN, 1>(out[0], w[r][2], w[r][3], s[1]);
-            if (has_nan)
-                nan_to_signed_zero<IN, OUT, NB>(w[r], out);
-            uint8_t *dst = data + (row * F) / 2 + (uint64_t)strip * (2 * NB);
-            if constexpr (NB == 2)
-                *reinterpret_cast<uint32_t *>(dst) = out[0];
-            else
-                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)out[0];
-        } else {
-            uint32_t out[NB];
-#pragma unroll
-            for (int b = 0; b < NB; b++)
-                out[b] = fp8x4<IN, OUT>(w[r][2 * b], w[r][2 * b + 1], s[b]);
-            if (has_nan)
-                nan_to_signed_zero<IN, OUT, NB>(w[r], out);
-            uint8_t *dst = data + row * F + (uint64_t)strip * (4 * NB);
-            if constexpr (NB == 2)
-                *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
-            else
-                *reinterpret_cast<uint32_t *>(dst) = out[0];
-        }
-    }
-
-    // Scale placement: logical row `group` goes to image row
-    // (group mod 4) + 32 * floor(group / 4).
-    const uint64_t slot = (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
-    uint8_t *sdst = scale + slot * (F / 4) + (uint64_t)strip * NB;
-    if constexpr (NB == 2)
-        *reinterpret_cast<uint16_t *>(sdst) = (uint16_t)(e[0] | (e[1] << 8));
-    else
-        *sdst = (uint8_t)e[0];
 }
 
 } // namespace mxq

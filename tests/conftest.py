@@ -16,5 +16,5 @@ def pytest_configure(config):
 
 
 def progress(msg: str) -> None:
-    """Name the case before a GPU step, flushed, so a lost box still says which."""
+    """Name the case before a GPU step, flushed, so a run that dies mid-step still names the case."""
     print("[case] " + msg, flush=True)
