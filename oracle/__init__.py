@@ -53,8 +53,9 @@ def _load():
                                       c.POINTER(c.c_float), c.POINTER(c.c_double))
         lib.mxq_oracle_quantize.argtypes = [P_u16, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int, P_u8, P_u8]
         lib.mxq_oracle_quantize.restype = c.c_int
-        lib.mxq_oracle_dequantize.argtypes = [P_u8, P_u8, c.c_int64, c.c_int64, c.c_int, P_f32]
+        lib.mxq_oracle_dequantize.argtypes = [P_u8, P_u8, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_void_p]
         lib.mxq_oracle_dequantize.restype = c.c_int
+        lib.mxq_oracle_f32_to_bf16_array.argtypes = [P_f32, c.c_int64, P_u16]
         lib.mxq_oracle_widen_array.argtypes = [P_u16, c.c_int64, c.c_int, P_f32]
         lib.mxq_oracle_narrow_array.argtypes = [P_f32, c.c_int64, c.c_int, P_u8]
         lib.mxq_oracle_prescale_array.argtypes = [P_f32, P_u8, c.c_int64, P_f32]
@@ -109,16 +110,29 @@ def quantize(x: np.ndarray, in_dtype: str, out_dtype: str, alt_emax: bool = Fals
     return data, image
 
 
-def dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, out_dtype: str) -> np.ndarray:
-    """Decode [P, F] fp32 values from packed data and the scale image."""
+RES_CODES = {"f32": 0, "bf16": 1}
+
+
+def dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, out_dtype: str,
+               res_dtype: str = "f32") -> np.ndarray:
+    """Decode [P, F] values from packed data and the scale image: float32, or
+    bf16 bit patterns (uint16) for ``res_dtype="bf16"``."""
     lib = _load()
     data = np.ascontiguousarray(data, dtype=np.uint8)
     image = np.ascontiguousarray(image, dtype=np.uint8)
-    out = np.empty((P, F), dtype=np.float32)
+    out = np.empty((P, F), dtype=np.float32 if res_dtype == "f32" else np.uint16)
     rc = lib.mxq_oracle_dequantize(_ptr(data, ctypes.c_uint8), _ptr(image, ctypes.c_uint8), P, F,
-                                   OUT_CODES[out_dtype], _ptr(out, ctypes.c_float))
+                                   OUT_CODES[out_dtype], RES_CODES[res_dtype], out.ctypes.data)
     if rc != 0:
         raise ValueError("oracle dequantize rejected the call (status %d)" % rc)
+    return out
+
+
+def f32_to_bf16(f: np.ndarray) -> np.ndarray:
+    lib = _load()
+    f = np.ascontiguousarray(f, dtype=np.float32).ravel()
+    out = np.empty(f.size, dtype=np.uint16)
+    lib.mxq_oracle_f32_to_bf16_array(_ptr(f, ctypes.c_float), f.size, _ptr(out, ctypes.c_uint16))
     return out
 
 

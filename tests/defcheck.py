@@ -139,3 +139,41 @@ def quantize(x: np.ndarray, in_dtype: str, fmt: str, alt: bool = False, image: n
         image = image.copy()
     image[scale_slot(np.arange(P // 8))] = e
     return data, image
+
+
+def unpack_codes(data: np.ndarray, P: int, F: int, fmt: str) -> np.ndarray:
+    """[P, F] element codes from packed data (FP4 via the golden container table)."""
+    if fmt != "e2m1":
+        return np.asarray(data, dtype=np.uint8).reshape(P, F)
+    tab = container_table()
+    d = np.asarray(data, dtype=np.uint8).reshape(P, F // 4, 2)
+    codes = np.zeros((P, F // 4, 4), dtype=np.uint8)
+    for k in range(4):
+        byte, hi = tab[k]
+        codes[:, :, k] = (d[:, :, byte] >> 4) if hi else (d[:, :, byte] & 0xF)
+    return codes.reshape(P, F)
+
+
+def decode_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """Values of codes (float64): the finite-code table with the sign bit;
+    e4m3fn 0x7F/0xFF and e5m2 0x7D-0x7F are NaN, e5m2 0x7C is Inf."""
+    f = FORMATS[fmt]
+    codes = np.asarray(codes, dtype=np.int64)
+    mag = codes & (f["signbit"] - 1)
+    sign = np.where(codes & f["signbit"], -1.0, 1.0)
+    vals = code_values(fmt)
+    table = np.full(f["signbit"], np.nan)
+    table[: vals.size] = vals
+    if fmt == "e5m2":
+        table[0x7C] = np.inf
+    return sign * table[mag]
+
+
+def dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, fmt: str) -> np.ndarray:
+    """float32 [P, F]: decode(q) * 2^(E8M0 - 127), exact in float64, rounded
+    once to float32 (numpy's own conversion)."""
+    codes = unpack_codes(data, P, F, fmt)
+    e = np.asarray(image, dtype=np.int64)[scale_slot(np.arange(P // 8))]      # [P/8, F/4]
+    e_full = np.repeat(np.repeat(e, 8, axis=0), 4, axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return (decode_codes(codes, fmt) * np.ldexp(1.0, e_full - 127)).astype(np.float32)

@@ -356,3 +356,62 @@ def test_bad_shapes_rejected():
 def test_empty_is_noop():
     d, im = oracle.quantize(np.zeros((0, 8), np.uint16), "bf16", "e4m3fn")
     assert d.size == 0 and im.size == 0
+
+
+# ------------------------------------------------------------------ dequantize
+
+def test_f32_to_bf16_matches_torch():
+    rng = np.random.default_rng(61)
+    u = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    # plus every tie and near-tie pattern around a few binades, denormals and the top of the range
+    base = np.array([0x3F800000, 0x00000000, 0x00010000, 0x7F7F0000, 0x80800000], np.uint32)
+    extra = (base[:, None] + np.arange(0, 0x30000, 0x4000, dtype=np.uint32)[None, :]).ravel()
+    extra = np.concatenate([extra, extra + 0x7FFF, extra + 0x8000, extra + 0x8001, extra + 0x18000])
+    f = np.concatenate([u, extra]).view(np.float32)
+    got = oracle.f32_to_bf16(f)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(f)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7FFF) > 0x7F80)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("P,F", [(8, 4), (16, 12), (40, 8), (64, 64)])
+def test_dequantize_equals_definition(fmt, P, F):
+    rng = np.random.default_rng(P * 31 + F)
+    data = rng.integers(0, 256, size=defcheck_data_bytes(P, F, fmt), dtype=np.uint8)
+    image = rng.integers(0, 256, size=(P, F // 4), dtype=np.uint8)
+    image[0, 0], image[min(1, P // 8 - 1) if P >= 16 else 0, -1] = 0, 255
+    got = oracle.dequantize(data, image, P, F, fmt, "f32")
+    ref = defcheck.dequantize(data, image, P, F, fmt)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    got16 = oracle.dequantize(data, image, P, F, fmt, "bf16")
+    ref16 = torch.from_numpy(ref.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got16[~nan], ref16[~nan])
+    assert np.all((got16[nan] & 0x7FFF) > 0x7F80)
+
+
+def defcheck_data_bytes(P, F, fmt):
+    return P * F // 2 if fmt == "e2m1" else P * F
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequantize_inverts_quantize_on_grid_values(fmt):
+    """Values already on the format's grid times 2^k, with the block max at
+    the top binade, come back exactly."""
+    P, F = 32, 32
+    rng = np.random.default_rng(62)
+    vals = defcheck.code_values(fmt)
+    k = rng.integers(-20, 20, size=(P // 8, 1, F // 4, 1))
+    pick = rng.integers(0, vals.size, size=(P // 8, 8, F // 4, 4))
+    sign = np.where(rng.integers(0, 2, size=pick.shape) == 1, -1.0, 1.0)
+    x = sign * vals[pick]
+    x[:, 0, :, 0] = vals[-1]                       # block max = format max
+    x = (x * np.ldexp(1.0, k)).reshape(P, F).astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    assert np.array_equal(workloads.bf16_bits_to_f32(bits), x)   # exact in bf16
+    data, image = oracle.quantize(bits, "bf16", fmt)
+    back = oracle.dequantize(data, image, P, F, fmt, "f32")
+    assert np.array_equal(back, x)
