@@ -2,6 +2,7 @@
 """Throughput of the MX quantize on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--op quantize|dequantize] [--res bf16|f32]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one full quantize of the workload tensor (one kernel launch: block
@@ -15,6 +16,10 @@ Prints one JSON line. ``value`` is algorithmic GB/s over the timed region:
 bytes per step = input (2 B/element) + data (1 B/element FP8, 0.5 B FP4) +
 logical scale (1/32 B/element); the never-written scale-image rows are not
 counted.
+
+``--op dequantize`` times the inverse instead: the workload is quantized once
+(untimed) and each step decodes it back to ``--res`` (bytes per step = data +
+logical scale + result).
 
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
@@ -35,11 +40,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MX quantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
+METRIC_DEQUANT = "MX dequantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16-131072x8192-colscaled"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
-                  "mx_microscaling_quantization_amd/csrc/mxq_api.hip"]
+KERNEL_SOURCES = {
+    "quantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
+                 "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
+    "dequantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
+                   "mx_microscaling_quantization_amd/csrc/mxq_dequantize_kernels.hpp",
+                   "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
+}
 
 
 def algorithmic_bytes(P: int, F: int, out: str) -> int:
@@ -48,24 +59,31 @@ def algorithmic_bytes(P: int, F: int, out: str) -> int:
     return 2 * n + data + n // 32
 
 
-def kernel_source_digest() -> str:
+def dequant_bytes(P: int, F: int, fmt: str, res: str) -> int:
+    n = P * F
+    data = n // 2 if fmt == "e2m1" else n
+    return data + n // 32 + n * (4 if res == "f32" else 2)
+
+
+def kernel_source_digest(op: str = "quantize") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[op]:
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, out: str):
+def recorded_traffic(workload: str, out: str, op: str = "quantize", res: str = ""):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, "quantize_%s_%s_hbm_traffic.txt" % (workload, out))
+    tag = "%s_%s_%s" % (op, workload, out) + ("_" + res if res else "")
+    path = os.path.join(PROFILES, "%s_hbm_traffic.txt" % tag)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
     m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not m_src or not m_b or m_src.group(1) != kernel_source_digest():
+    if not m_src or not m_b or m_src.group(1) != kernel_source_digest(op):
         return None
     return float(m_b.group(1))
 
@@ -111,6 +129,28 @@ def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows:
                       % (done_rows, P, done_rows, F, spent)}
 
 
+def cpu_baseline_dequant(data, image, fmt: str, res: str, budget_s: float = 12.0, slab_rows: int = 4096):
+    """The CPU oracle's dequantize (single thread) on leading row slabs."""
+    import oracle
+
+    oracle.build(force=False)
+    P = data.shape[0]
+    F = image.shape[1] * 4
+    done_rows, spent = 0, 0.0
+    while done_rows < P and spent < budget_s:
+        rows = min(slab_rows, P - done_rows)
+        d = data[done_rows:done_rows + rows].cpu().numpy()
+        im = image[done_rows:done_rows + rows].cpu().numpy()   # slabs start at multiples of 32 rows
+        t0 = time.perf_counter()
+        oracle.dequantize(d, im, rows, F, fmt, res)
+        spent += time.perf_counter() - t0
+        done_rows += rows
+    nbytes = dequant_bytes(done_rows, F, fmt, res)
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d rows (%d x %d, %.3g s of single-thread oracle time)"
+                      % (done_rows, P, done_rows, F, spent)}
+
+
 def copy_calibration(steps: int, warmup: int) -> None:
     import torch
 
@@ -138,6 +178,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--out", default=None, help="output format (default: the workload's first)")
+    ap.add_argument("--op", choices=("quantize", "dequantize"), default="quantize")
+    ap.add_argument("--res", choices=("bf16", "f32"), default="bf16", help="dequantize result type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -169,9 +211,23 @@ def main() -> int:
     data = torch.empty(mxq.data_shape(P, F, out), dtype=torch.uint8, device=dev)
     image = torch.zeros(mxq.scale_image_shape(P, F), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.op == "quantize":
+        def step():
+            mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+        nbytes = algorithmic_bytes(P, F, out)
+    else:
+        mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+        torch.cuda.synchronize()
+        del xt
+        res_t = torch.bfloat16 if args.res == "bf16" else torch.float32
+        result = torch.empty((P, F), dtype=res_t, device=dev)
+
+        def step():
+            mxq.dequantize(data, image, out, res_t, out=result, stream=stream)
+        nbytes = dequant_bytes(P, F, out, args.res)
 
     for _ in range(args.warmup):
-        mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+        step()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -181,7 +237,7 @@ def main() -> int:
     t_begin.record(stream)
     for k in range(args.steps):
         starts[k].record(stream)
-        mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+        step()
         ends[k].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -189,13 +245,20 @@ def main() -> int:
     total_ms = t_begin.elapsed_time(t_end)
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
-    nbytes = algorithmic_bytes(P, F, out)
     value = nbytes * args.steps / (total_ms * 1e-3) / 1e9
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(args.workload, out)
+    if args.op == "quantize":
+        traffic = recorded_traffic(args.workload, out)
+    else:
+        traffic = recorded_traffic(args.workload, out, "dequantize", args.res)
 
+    config = {"workload": args.workload, "P": P, "F": F, "in": spec["in_dtype"], "out": out,
+              "bytes_per_step": nbytes, "elements_per_step": P * F}
+    if args.op == "dequantize":
+        config = {"workload": args.workload + "-dequantize", "P": P, "F": F, "in": out, "out": args.res,
+                  "bytes_per_step": nbytes, "elements_per_step": P * F}
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.op == "quantize" else METRIC_DEQUANT,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -205,10 +268,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": spec["in_dtype"],
+        "dtype": spec["in_dtype"] if args.op == "quantize" else out,
         "data": "synthetic",
-        "config": {"workload": args.workload, "P": P, "F": F, "in": spec["in_dtype"], "out": out,
-                   "bytes_per_step": nbytes, "elements_per_step": P * F},
+        "config": config,
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "elements_per_s": round(P * F * args.steps / (total_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -217,7 +279,10 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"])
+        if args.op == "quantize":
+            result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"])
+        else:
+            result["cpu_baseline"] = cpu_baseline_dequant(data, image, out, args.res)
     print(json.dumps(result), flush=True)
     return 0
 

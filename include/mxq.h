@@ -71,8 +71,12 @@ enum mxq_status {
     MXQ_E_ALIGN = 6,     /* a buffer pointer is not 16-byte aligned           */
     MXQ_E_OVERFLOW = 7,  /* P*F too large for this library's index range      */
     MXQ_E_HIP = 8,       /* the HIP runtime refused the launch                */
-    MXQ_E_FLAGS = 9      /* unknown bits in a flags argument                  */
+    MXQ_E_FLAGS = 9,     /* unknown bits in a flags argument                  */
+    MXQ_E_RES_DTYPE = 10 /* dequantize result type is not F32 or BF16         */
 };
+
+/* Result types of mxq_dequantize. */
+enum mxq_res_dtype { MXQ_RES_F32 = 0, MXQ_RES_BF16 = 1 };
 
 /*
  * mxq_quantize -- the MX quantize of one P x F tensor.
@@ -106,6 +110,38 @@ size_t mxq_data_bytes(int64_t P, int64_t F, int out_dtype);
 /* Bytes of the scale image: P*F/4 (P rows of F/4 bytes, one in eight of them
  * written). 0 for invalid arguments. */
 size_t mxq_scale_image_bytes(int64_t P, int64_t F);
+
+/*
+ * mxq_dequantize -- decode an MX-quantized P x F tensor back to F32 or BF16.
+ *
+ * The inverse the consumer of the quantize applies: "MX Microscaling:
+ * Quantize, Block-Scaling and E8M0", quantizeDataApplyingMxScales (each
+ * decoded element times 2^(E8M0 - 127), an fp32 ldexpf), reading the E8M0
+ * byte from the placed scale row ("E8M0 Scale-Tensor Layout") and FP4 codes
+ * through the same container lane order ("FP4 x4-Pack and Intra-x4 Lane
+ * Order"). Element codes decode by the OCP definitions: e4m3fn 0x7F/0xFF and
+ * e5m2 0x7D..0x7F / 0xFD..0xFF are NaN, e5m2 0x7C / 0xFC are +-Inf.
+ *
+ *   data       device pointer, layout and size as mxq_quantize's data_out
+ *              for format `fmt` (enum mxq_out_dtype), 16-byte aligned.
+ *   scale_in   device pointer, a P x F/4 scale image as mxq_quantize writes
+ *              it; only the placed rows are read. 16-byte aligned.
+ *   P, F       as for mxq_quantize (P % 8 == 0, F % 4 == 0; empty is a no-op).
+ *   res_dtype  enum mxq_res_dtype. F32: decode(q) * 2^(E8M0 - 127) rounded
+ *              once to fp32 (overflow gives +-Inf; exact otherwise). BF16:
+ *              that fp32 value rounded to nearest-even bf16.
+ *   out        device pointer, mxq_result_bytes(P, F, res_dtype) bytes,
+ *              16-byte aligned, row-major P x F; fully overwritten.
+ *   stream     hipStream_t of the current device (NULL = default stream).
+ *
+ * Returns MXQ_OK once enqueued, else an MXQ_E_* code with nothing enqueued.
+ */
+int mxq_dequantize(const void *data, const void *scale_in, int64_t P, int64_t F, int fmt, int res_dtype,
+                   void *out, void *stream);
+
+/* Bytes of the dequantize result: P*F*4 (F32) or P*F*2 (BF16); 0 for
+ * invalid arguments. */
+size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype);
 
 /* Human-readable message for a status code (static storage, never NULL). */
 const char *mxq_status_string(int status);

@@ -16,8 +16,9 @@ import threading
 import torch  # loaded first so that the library binds to torch's HIP runtime
 
 __all__ = [
-    "IN_DTYPES", "OUT_DTYPES", "MXQError", "quantize", "data_bytes", "scale_image_bytes",
-    "data_shape", "scale_image_shape", "logical_scale_view", "status_string", "library_path", "load",
+    "IN_DTYPES", "OUT_DTYPES", "RES_DTYPES", "MXQError", "quantize", "dequantize", "data_bytes",
+    "scale_image_bytes", "result_bytes", "data_shape", "scale_image_shape", "logical_scale_view",
+    "status_string", "library_path", "load",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,6 +26,7 @@ _LIB_NAME = "libmxq.so"
 
 IN_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 OUT_DTYPES = {"e4m3fn": 0, "e5m2": 1, "e2m1": 2}
+RES_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 ABI_VERSION = 1
 
 _lock = threading.Lock()
@@ -61,6 +63,11 @@ def load():
         lib.mxq_data_bytes.restype = c.c_size_t
         lib.mxq_scale_image_bytes.argtypes = [c.c_int64, c.c_int64]
         lib.mxq_scale_image_bytes.restype = c.c_size_t
+        lib.mxq_dequantize.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int,
+                                       c.c_void_p, c.c_void_p]
+        lib.mxq_dequantize.restype = c.c_int
+        lib.mxq_result_bytes.argtypes = [c.c_int64, c.c_int64, c.c_int]
+        lib.mxq_result_bytes.restype = c.c_size_t
         lib.mxq_status_string.argtypes = [c.c_int]
         lib.mxq_status_string.restype = c.c_char_p
         lib.mxq_abi_version.argtypes = []
@@ -93,6 +100,10 @@ def data_bytes(P: int, F: int, out_dtype: str) -> int:
 
 def scale_image_bytes(P: int, F: int) -> int:
     return int(load().mxq_scale_image_bytes(P, F))
+
+
+def result_bytes(P: int, F: int, res_dtype: torch.dtype) -> int:
+    return int(load().mxq_result_bytes(P, F, RES_DTYPES[res_dtype]))
 
 
 def data_shape(P: int, F: int, out_dtype: str):
@@ -148,3 +159,40 @@ def quantize(x: torch.Tensor, out_dtype: str = "e4m3fn", data_out: torch.Tensor 
         _check(lib.mxq_quantize(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, data_out.data_ptr(),
                                 scale_out.data_ptr(), stream.cuda_stream))
     return data_out, scale_out
+
+
+def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "e4m3fn",
+               res_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+               stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Decode MX data back to [P, F] float32 or bfloat16.
+
+    ``data`` is the uint8 data output of :func:`quantize` for format
+    ``out_dtype`` ([P, F] FP8 or [P, F/2] FP4) and ``scale_image`` its
+    [P, F/4] scale image. Each result is decode(code) * 2^(E8M0 - 127),
+    rounded once to float32 (then nearest-even to bfloat16).
+    """
+    lib = load()
+    code = _out_code(out_dtype)
+    if res_dtype not in RES_DTYPES:
+        raise MXQError(10, "result type must be float32 or bfloat16, got %s" % res_dtype)
+    if data.dim() != 2 or scale_image.dim() != 2:
+        raise ValueError("data and scale_image must be 2-D")
+    if not data.is_cuda or scale_image.device != data.device:
+        raise ValueError("data and scale_image must be device tensors on one device")
+    if not (data.is_contiguous() and scale_image.is_contiguous()):
+        raise ValueError("data and scale_image must be contiguous")
+    P = data.shape[0]
+    F = scale_image.shape[1] * 4
+    if tuple(data.shape) != data_shape(P, F, out_dtype) or tuple(scale_image.shape) != scale_image_shape(P, F):
+        raise ValueError("data %s / scale_image %s do not describe one [P, F] tensor in format %s"
+                         % (tuple(data.shape), tuple(scale_image.shape), out_dtype))
+    if out is None:
+        out = torch.empty((P, F), dtype=res_dtype, device=data.device)
+    elif out.dtype != res_dtype or tuple(out.shape) != (P, F) or not out.is_contiguous() or out.device != data.device:
+        raise ValueError("out must be a contiguous [%d, %d] %s tensor on %s" % (P, F, res_dtype, data.device))
+    if stream is None:
+        stream = torch.cuda.current_stream(data.device)
+    with torch.cuda.device(data.device):
+        _check(lib.mxq_dequantize(data.data_ptr(), scale_image.data_ptr(), P, F, code, RES_DTYPES[res_dtype],
+                                  out.data_ptr(), stream.cuda_stream))
+    return out

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "mxq.h"
+#include "mxq_dequantize_kernels.hpp"
 #include "mxq_quantize_kernels.hpp"
 
 namespace {
@@ -43,6 +44,23 @@ template <int IN> kernel_fn pick_out(int out_dtype, int nb)
     }
 }
 
+typedef void (*dq_kernel_fn)(const uint8_t *, const uint8_t *, void *, uint64_t, uint32_t, uint32_t);
+
+template <int FMT, int RES> dq_kernel_fn dq_pick_nb(int nb)
+{
+    return nb == 2 ? (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 2, kNonTemporal>
+                   : (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 1, kNonTemporal>;
+}
+
+template <int RES> dq_kernel_fn dq_pick_fmt(int fmt, int nb)
+{
+    switch (fmt) {
+    case MXQ_OUT_E4M3FN: return dq_pick_nb<mxq::kOutE4M3FN, RES>(nb);
+    case MXQ_OUT_E5M2: return dq_pick_nb<mxq::kOutE5M2, RES>(nb);
+    default: return dq_pick_nb<mxq::kOutE2M1, RES>(nb);
+    }
+}
+
 int check_shape(int64_t P, int64_t F)
 {
     if (P < 0 || P % 8 != 0)
@@ -75,6 +93,7 @@ const char *mxq_status_string(int status)
     case MXQ_E_OVERFLOW: return "tensor too large for the library's index range";
     case MXQ_E_HIP: return "the HIP runtime rejected the kernel launch";
     case MXQ_E_FLAGS: return "unknown flag bits";
+    case MXQ_E_RES_DTYPE: return "dequantize result type must be F32 or BF16";
     default: return "unknown status";
     }
 }
@@ -96,6 +115,57 @@ size_t mxq_scale_image_bytes(int64_t P, int64_t F)
     if (check_shape(P, F) != MXQ_OK)
         return 0;
     return (size_t)(P * (F / 4));
+}
+
+size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype)
+{
+    if (check_shape(P, F) != MXQ_OK)
+        return 0;
+    switch (res_dtype) {
+    case MXQ_RES_F32: return (size_t)(P * F) * 4;
+    case MXQ_RES_BF16: return (size_t)(P * F) * 2;
+    default: return 0;
+    }
+}
+
+int mxq_dequantize(const void *data, const void *scale_in, int64_t P, int64_t F, int fmt, int res_dtype,
+                   void *out, void *stream)
+{
+    if (fmt != MXQ_OUT_E4M3FN && fmt != MXQ_OUT_E5M2 && fmt != MXQ_OUT_E2M1)
+        return MXQ_E_OUT_DTYPE;
+    if (res_dtype != MXQ_RES_F32 && res_dtype != MXQ_RES_BF16)
+        return MXQ_E_RES_DTYPE;
+    int rc = check_shape(P, F);
+    if (rc != MXQ_OK)
+        return rc;
+    if (F > 0 && P > INT64_MAX / 4 / F)
+        return MXQ_E_OVERFLOW; // fp32 result bytes P*F*4 must fit
+    if (P == 0 || F == 0)
+        return MXQ_OK;
+    if (!data || !scale_in || !out)
+        return MXQ_E_NULL;
+    if (((uintptr_t)data | (uintptr_t)scale_in | (uintptr_t)out) & 15u)
+        return MXQ_E_ALIGN;
+
+    const int nb = (F % 8 == 0) ? 2 : 1;
+    const int64_t nstrips = F / (4 * nb);
+    const int64_t tiles_per_group = (nstrips + kThreads - 1) / kThreads;
+    const int64_t groups = P / 8;
+    if (groups > kMaxWorkgroups / tiles_per_group)
+        return MXQ_E_OVERFLOW;
+
+    dq_kernel_fn k = res_dtype == MXQ_RES_F32 ? dq_pick_fmt<mxq::kResF32>(fmt, nb)
+                                              : dq_pick_fmt<mxq::kResBF16>(fmt, nb);
+    const uint8_t *a0 = (const uint8_t *)data;
+    const uint8_t *a1 = (const uint8_t *)scale_in;
+    void *a2 = out;
+    uint64_t a3 = (uint64_t)F;
+    uint32_t a4 = (uint32_t)nstrips;
+    uint32_t a5 = (uint32_t)tiles_per_group;
+    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5};
+    hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(groups * tiles_per_group)), dim3(kThreads),
+                                     args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
 }
 
 int mxq_quantize(const void *in, int64_t P, int64_t F, int in_dtype, int out_dtype, void *data_out,

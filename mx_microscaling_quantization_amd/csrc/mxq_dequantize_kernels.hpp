@@ -1,0 +1,211 @@
+// mxq_dequantize_kernels.hpp -- gfx950 kernels of the MX dequantize.
+//
+// The inverse the consumer applies ("MX Microscaling: Quantize,
+// Block-Scaling and E8M0", quantizeDataApplyingMxScales: the dequant side
+// multiplies each decoded element by 2^(E8M0 - 127) with an fp32 ldexpf; the
+// E8M0 byte is read back from the placed scale row and FP4 nibbles through
+// the same container lane order).
+//
+// Same work split as the quantize: a thread owns an 8-row strip of NB
+// blocks; it reads the strip's NB scale bytes once from the placed image row
+// and 4*NB codes (FP8) or 2*NB bytes (FP4) per row, and writes 4*NB results
+// per row. gfx950's v_cvt_scalef32_pk_{f32,bf16}_{fp8,bf8,fp4} compute
+// decode(q) * scale for two codes at once and round once to the result type,
+// which is exactly ldexpf (then nearest-even to bf16); the scale operand is
+// the fp32 2^(E8M0 - 127): a normal number for E8M0 1..254 and the denormal
+// 2^-127 for E8M0 0. E8M0 255 (2^128) is not an fp32 number, so such a block
+// takes a rarely used branch that applies 2^127 and then doubles (exact:
+// the scaled value has at most four significant bits).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxq_quantize_kernels.hpp"
+
+namespace mxq {
+
+enum { kResF32 = 0, kResBF16 = 1 };
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 scale operand for an E8M0 byte in 0..254 (255 handled by the caller).
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t e)
+{
+    return __uint_as_float(e == 0 ? 0x00400000u : (e << 23));
+}
+
+// Nearest-even fp32 -> bf16 of a value (used only on the E8M0-255 branch).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t b = __float_as_uint(f);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u)
+        return (b >> 16) | 0x40u;
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Two results from two codes. FP8: the codes are bytes 2*HI, 2*HI+1 of `w`.
+// FP4: the codes are the low and high nibble of byte SEL of `w`.
+// RES f32: r[0], r[1] are the two fp32 bit patterns; bf16: r[0] holds both.
+template <int FMT, int RES, int SEL>
+__device__ __forceinline__ void decode2(uint32_t w, float s, uint32_t *r)
+{
+    if constexpr (RES == kResF32) {
+        f32x2_t v;
+        if constexpr (FMT == kOutE4M3FN)
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, s, SEL != 0);
+        else if constexpr (FMT == kOutE5M2)
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, s, SEL != 0);
+        else
+            v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, SEL);
+        r[0] = __float_as_uint(v.x);
+        r[1] = __float_as_uint(v.y);
+    } else {
+        bf16x2_t v;
+        if constexpr (FMT == kOutE4M3FN)
+            v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, SEL != 0);
+        else if constexpr (FMT == kOutE5M2)
+            v = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, s, SEL != 0);
+        else
+            v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, SEL);
+        r[0] = __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// Decode the four codes of one block into four results (element order
+// e0..e3). `w` holds the block's codes: FP8 -- the whole u32 lane (e_k in
+// byte k); FP4 -- the dword holding the block's 16-bit container at byte
+// offset 2*HALF (byte 2*HALF+1 = e0 | e1 << 4, byte 2*HALF = e2 | e3 << 4).
+// out: f32 -> 4 words; bf16 -> 2 words.
+template <int FMT, int RES, int HALF>
+__device__ __forceinline__ void decode_block(uint32_t w, float s, uint32_t *out)
+{
+    constexpr int step = RES == kResF32 ? 2 : 1;
+    if constexpr (FMT == kOutE2M1) {
+        decode2<FMT, RES, 2 * HALF + 1>(w, s, out);      // e0, e1
+        decode2<FMT, RES, 2 * HALF>(w, s, out + step);   // e2, e3
+    } else {
+        decode2<FMT, RES, 0>(w, s, out);                 // bytes 0, 1
+        decode2<FMT, RES, 1>(w, s, out + step);          // bytes 2, 3
+    }
+}
+
+// The E8M0 = 255 block: decode with 2^127, then double, then round.
+template <int FMT, int RES, int HALF>
+__device__ __forceinline__ void decode_block_e255(uint32_t w, uint32_t *out)
+{
+    uint32_t f[4];
+    decode_block<FMT, kResF32, HALF>(w, __uint_as_float(254u << 23), f);
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+        f[k] = __float_as_uint(__uint_as_float(f[k]) * 2.0f);
+    if constexpr (RES == kResF32) {
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            out[k] = f[k];
+    } else {
+        out[0] = f32_to_bf16_bits(__uint_as_float(f[0])) | (f32_to_bf16_bits(__uint_as_float(f[1])) << 16);
+        out[1] = f32_to_bf16_bits(__uint_as_float(f[2])) | (f32_to_bf16_bits(__uint_as_float(f[3])) << 16);
+    }
+}
+
+// The dequantize kernel. Grid as the quantize (GPT = 1): one workgroup per
+// (row group, run of blockDim.x strips).
+//   data    FP8: P*F bytes; FP4: P*F/2 bytes
+//   scale   the P x F/4 scale image (only the placed rows are read)
+//   out     P x F results, fp32 or bf16
+template <int FMT, int RES, int NB, int NT>
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restrict__ data,
+                                                         const uint8_t *__restrict__ scale,
+                                                         void *__restrict__ out, uint64_t F,
+                                                         uint32_t nstrips, uint32_t tiles_per_band)
+{
+    static_assert(NB == 1 || NB == 2, "a strip is 1 or 2 blocks");
+    constexpr int LD = NT & 1, ST = (NT >> 1) & 1;
+    constexpr int RES_BYTES = RES == kResF32 ? 4 : 2;
+    const uint32_t group = blockIdx.x / tiles_per_band;
+    const uint32_t strip = (blockIdx.x - group * tiles_per_band) * blockDim.x + threadIdx.x;
+    if (strip >= nstrips)
+        return;
+
+    // the strip's E8M0 bytes, from logical row `group`'s placed image row
+    const uint64_t slot = (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
+    const uint8_t *srow = scale + slot * (F / 4) + (uint64_t)strip * NB;
+    uint32_t e[NB];
+    if constexpr (NB == 2) {
+        const uint32_t two = load<LD>(reinterpret_cast<const uint16_t *>(srow));
+        e[0] = two & 0xFFu;
+        e[1] = two >> 8;
+    } else {
+        e[0] = load<LD>(srow);
+    }
+    float s[NB];
+    bool any255 = false;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        any255 |= e[b] == 255u;
+        s[b] = e8m0_scale_operand(e[b] & 0xFFu);
+    }
+
+    // codes of all 8 rows first, then convert and store row by row
+    uint32_t c[8][NB];
+    const uint64_t row0 = (uint64_t)group * 8u;
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        const uint64_t row = row0 + r;
+        if constexpr (FMT == kOutE2M1) {
+            const uint8_t *p = data + (row * F) / 2 + (uint64_t)strip * (2 * NB);
+            if constexpr (NB == 2)
+                c[r][0] = load<LD>(reinterpret_cast<const uint32_t *>(p));
+            else
+                c[r][0] = load<LD>(reinterpret_cast<const uint16_t *>(p));
+        } else {
+            const uint8_t *p = data + row * F + (uint64_t)strip * (4 * NB);
+            if constexpr (NB == 2) {
+                u32x2_t v = load<LD>(reinterpret_cast<const u32x2_t *>(p));
+                c[r][0] = v.x;
+                c[r][1] = v.y;
+            } else {
+                c[r][0] = load<LD>(reinterpret_cast<const uint32_t *>(p));
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        const uint64_t row = row0 + r;
+        uint32_t res[NB * RES_BYTES]; // 4*NB results of RES_BYTES each, in words
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const uint32_t w = FMT == kOutE2M1 ? c[r][0] : c[r][b];
+            uint32_t *dst = res + b * (RES_BYTES);
+            if (b == 0)
+                decode_block<FMT, RES, 0>(w, s[b], dst);
+            else
+                decode_block<FMT, RES, 1>(w, s[b], dst);
+        }
+        if (any255) {
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                if (e[b] != 255u)
+                    continue;
+                const uint32_t w = FMT == kOutE2M1 ? c[r][0] : c[r][b];
+                if (b == 0)
+                    decode_block_e255<FMT, RES, 0>(w, res + b * RES_BYTES);
+                else
+                    decode_block_e255<FMT, RES, 1>(w, res + b * RES_BYTES);
+            }
+        }
+        uint8_t *dst = reinterpret_cast<uint8_t *>(out) + (row * F + (uint64_t)strip * (4 * NB)) * RES_BYTES;
+        if constexpr (NB * RES_BYTES == 8) { // 32 bytes: fp32, two blocks
+            u32x4_t lo = {res[0], res[1], res[2], res[3]};
+            u32x4_t hi = {res[4], res[5], res[6], res[7]};
+            store<ST>(reinterpret_cast<u32x4_t *>(dst), lo);
+            store<ST>(reinterpret_cast<u32x4_t *>(dst) + 1, hi);
+        } else {
+            store_bytes<4 * NB * RES_BYTES, ST>(dst, res);
+        }
+    }
+}
+
+} // namespace mxq

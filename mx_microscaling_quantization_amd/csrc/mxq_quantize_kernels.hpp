@@ -150,8 +150,10 @@ __device__ __forceinline__ uint32_t fp4_bit_offset(uint32_t k)
 }
 
 // Rewrite the codes of NaN elements to a zero of the NaN's sign. `w` holds
-// the input dwords of one row (2*NB of them), `out` the row's output codes:
-// FP8 in out[0..NB-1] (byte k of the strip = element k), FP4 in out[0].
+// the input dwords of one row of a strip (2*NB of them, element k in the
+// 16-bit half k&1 of w[k/2]); `out` the row's output codes: FP8 byte k of
+// the strip is byte k&3 of out[k/4]; FP4 element k is in out[k/8] at
+// fp4_bit_offset(k mod 8).
 template <int IN, int OUT, int NB>
 __device__ __forceinline__ void nan_to_signed_zero(const uint32_t *w, uint32_t *out)
 {
@@ -162,8 +164,8 @@ __device__ __forceinline__ void nan_to_signed_zero(const uint32_t *w, uint32_t *
             continue;
         uint32_t sign = h >> 15;
         if constexpr (OUT == kOutE2M1) {
-            uint32_t sh = fp4_bit_offset(k);
-            out[0] = (out[0] & ~(0xFu << sh)) | ((sign << 3) << sh);
+            uint32_t sh = fp4_bit_offset(k & 7);
+            out[k >> 3] = (out[k >> 3] & ~(0xFu << sh)) | ((sign << 3) << sh);
         } else {
             uint32_t sh = 8 * (k & 3);
             out[k >> 2] = (out[k >> 2] & ~(0xFFu << sh)) | ((sign << 7) << sh);
@@ -173,13 +175,6 @@ __device__ __forceinline__ void nan_to_signed_zero(const uint32_t *w, uint32_t *
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-template <int NB> struct Vec;
-template <> struct Vec<2> { typedef u32x4_t type; };
-template <> struct Vec<1> { typedef u32x2_t type; };
-
-__device__ __forceinline__ void unpack(const u32x4_t &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; }
-__device__ __forceinline__ void unpack(const u32x2_t &v, uint32_t *w) { w[0] = v.x; w[1] = v.y; }
 
 // Loads and stores with an optional non-temporal hint (streaming data that
 // no later access of this kernel touches again).
@@ -198,18 +193,45 @@ template <int NT, typename T> __device__ __forceinline__ void store(T *p, T v)
         *p = v;
 }
 
-// The quantize kernel.
-//
-// Grid: one workgroup per (band, run of up to blockDim.x strips), where a
-// band is GPT consecutive row groups and `tiles_per_band` runs cover a band.
-// Each thread quantizes the same strip in every row group of its band; all
-// 8*GPT row loads are issued before any arithmetic. NT bit 0 marks the loads
-// non-temporal, bit 1 the stores. XCD != 0 renumbers workgroups so that each
-// of the XCD chiplets (which receive workgroups round-robin) walks one
-// contiguous range of tiles.
-//   F          columns (pitch of the input and of FP8 data), F % (4*NB) == 0
-//   nstrips    F / (4*NB)
-//   ngroups    P / 8
+// One row of a strip: 4*NB input elements = 2*NB dwords, fetched as one
+// 8-byte (NB = 1) or NB/2 16-byte loads.
+template <int NB, int NT> __device__ __forceinline__ void load_row(const uint16_t *row, uint32_t strip, uint32_t *w)
+{
+    if constexpr (NB == 1) {
+        u32x2_t v = load<NT>(reinterpret_cast<const u32x2_t *>(row) + strip);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+        const u32x4_t *p = reinterpret_cast<const u32x4_t *>(row) + (uint64_t)strip * (NB / 2);
+#pragma unroll
+        for (int i = 0; i < NB / 2; i++) {
+            u32x4_t v = load<NT>(p + i);
+            w[4 * i + 0] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
+        }
+    }
+}
+
+// Store NBYTES (2, 4, 8 or 16) bytes held in out[] to dst (NBYTES-aligned).
+template <int NBYTES, int NT> __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *out)
+{
+    if constexpr (NBYTES == 1) {
+        store<NT>(dst, (uint8_t)out[0]);
+    } else if constexpr (NBYTES == 2) {
+        store<NT>(reinterpret_cast<uint16_t *>(dst), (uint16_t)out[0]);
+    } else if constexpr (NBYTES == 4) {
+        store<NT>(reinterpret_cast<uint32_t *>(dst), out[0]);
+    } else if constexpr (NBYTES == 8) {
+        u32x2_t v = {out[0], out[1]};
+        store<NT>(reinterpret_cast<u32x2_t *>(dst), v);
+    } else {
+        u32x4_t v = {out[0], out[1], out[2], out[3]};
+        store<NT>(reinterpret_cast<u32x4_t *>(dst), v);
+    }
+}
+
 template <int XCD> __device__ __forceinline__ uint32_t tile_index()
 {
     if constexpr (XCD == 0) {
@@ -223,6 +245,19 @@ template <int XCD> __device__ __forceinline__ uint32_t tile_index()
     }
 }
 
+// The quantize kernel.
+//
+// Grid: one workgroup per (band, run of up to blockDim.x strips), where a
+// band is GPT consecutive row groups and `tiles_per_band` runs cover a band.
+// A strip is NB blocks side by side (4*NB columns, F % (4*NB) == 0). Each
+// thread quantizes the same strip in every row group of its band; all 8*GPT
+// rows are loaded before any arithmetic. NT bit 0 marks the loads
+// non-temporal, bit 1 the stores. XCD != 0 renumbers workgroups so that each
+// of the XCD chiplets (which receive workgroups round-robin) walks one
+// contiguous range of tiles.
+//   F          columns (pitch of the input and of FP8 data)
+//   nstrips    F / (4*NB)
+//   ngroups    P / 8
 template <int IN, int OUT, int NB, int GPT, int NT, int XCD = 0>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ in,
                                                        uint8_t *__restrict__ data,
@@ -230,14 +265,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
                                                        uint64_t F, uint32_t nstrips,
                                                        uint32_t tiles_per_band, uint32_t ngroups)
 {
-    typedef typename Vec<NB>::type vec_t;
+    static_assert(NB == 1 || NB == 2 || NB == 4, "a strip is 1, 2 or 4 blocks");
+    constexpr int LD = NT & 1, ST = (NT >> 1) & 1;
     const uint32_t tile = tile_index<XCD>();
     const uint32_t band = tile / tiles_per_band;
     const uint32_t strip = (tile - band * tiles_per_band) * blockDim.x + threadIdx.x;
     if (strip >= nstrips)
         return;
 
-    const uint64_t pitch = F / (4 * NB); // row pitch in vec_t units
     const uint32_t g0 = band * GPT;
 
     uint32_t w[GPT][8][2 * NB];
@@ -245,10 +280,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
     for (int j = 0; j < GPT; j++) {
         if (GPT > 1 && g0 + j >= ngroups)
             break;
-        const vec_t *src = reinterpret_cast<const vec_t *>(in + (uint64_t)(g0 + j) * 8u * F) + strip;
+        const uint16_t *rows = in + (uint64_t)(g0 + j) * 8u * F;
 #pragma unroll
         for (int r = 0; r < 8; r++)
-            unpack(load<NT & 1>(src + r * pitch), w[j][r]);
+            load_row<NB, LD>(rows + r * F, strip, w[j][r]);
     }
 
 #pragma unroll
@@ -280,17 +315,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
         for (int r = 0; r < 8; r++) {
             const uint64_t row = row0 + r;
             if constexpr (OUT == kOutE2M1) {
-                uint32_t out[1] = {0};
-                out[0] = fp4_container<IN, 0>(out[0], w[j][r][0], w[j][r][1], s[0]);
-                if constexpr (NB == 2)
-                    out[0] = fp4_container<IN, 1>(out[0], w[j][r][2], w[j][r][3], s[1]);
+                // two blocks (two containers) per output dword
+                uint32_t out[(NB + 1) / 2];
+#pragma unroll
+                for (int h = 0; h < (NB + 1) / 2; h++) {
+                    out[h] = fp4_container<IN, 0>(0u, w[j][r][4 * h], w[j][r][4 * h + 1], s[2 * h]);
+                    if constexpr (NB > 1)
+                        out[h] = fp4_container<IN, 1>(out[h], w[j][r][4 * h + 2], w[j][r][4 * h + 3], s[2 * h + 1]);
+                }
                 if (has_nan)
                     nan_to_signed_zero<IN, OUT, NB>(w[j][r], out);
-                uint8_t *dst = data + (row * F) / 2 + (uint64_t)strip * (2 * NB);
-                if constexpr (NB == 2)
-                    store<(NT >> 1) & 1>(reinterpret_cast<uint32_t *>(dst), out[0]);
-                else
-                    store<(NT >> 1) & 1>(reinterpret_cast<uint16_t *>(dst), (uint16_t)out[0]);
+                store_bytes<2 * NB, ST>(data + (row * F) / 2 + (uint64_t)strip * (2 * NB), out);
             } else {
                 uint32_t out[NB];
 #pragma unroll
@@ -298,24 +333,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
                     out[b] = fp8x4<IN, OUT>(w[j][r][2 * b], w[j][r][2 * b + 1], s[b]);
                 if (has_nan)
                     nan_to_signed_zero<IN, OUT, NB>(w[j][r], out);
-                uint8_t *dst = data + row * F + (uint64_t)strip * (4 * NB);
-                if constexpr (NB == 2) {
-                    u32x2_t v = {out[0], out[1]};
-                    store<(NT >> 1) & 1>(reinterpret_cast<u32x2_t *>(dst), v);
-                } else {
-                    store<(NT >> 1) & 1>(reinterpret_cast<uint32_t *>(dst), out[0]);
-                }
+                store_bytes<4 * NB, ST>(data + row * F + (uint64_t)strip * (4 * NB), out);
             }
         }
 
         // Scale placement: logical row `group` goes to image row
         // (group mod 4) + 32 * floor(group / 4).
         const uint64_t slot = (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
-        uint8_t *sdst = scale + slot * (F / 4) + (uint64_t)strip * NB;
-        if constexpr (NB == 2)
-            store<(NT >> 1) & 1>(reinterpret_cast<uint16_t *>(sdst), (uint16_t)(e[0] | (e[1] << 8)));
-        else
-            store<(NT >> 1) & 1>(sdst, (uint8_t)e[0]);
+        uint32_t packed[1] = {0};
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+            packed[0] |= e[b] << (8 * b);
+        store_bytes<NB, ST>(scale + slot * (F / 4) + (uint64_t)strip * NB, packed);
     }
 }
 

@@ -35,8 +35,8 @@ def _header_enums():
 def test_library_exports_every_declared_function():
     lib = mxq.load()
     names = _declared_functions()
-    assert {"mxq_quantize", "mxq_data_bytes", "mxq_scale_image_bytes", "mxq_status_string",
-            "mxq_abi_version"} <= set(names)
+    assert {"mxq_quantize", "mxq_dequantize", "mxq_data_bytes", "mxq_scale_image_bytes", "mxq_result_bytes",
+            "mxq_status_string", "mxq_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     # and the shared object's dynamic symbol table has them as functions
@@ -103,6 +103,37 @@ def test_validation_errors_before_launch():
     assert _call(good + 8, 16, 8, 0, 0, good, good) == e["MXQ_E_ALIGN"]
     assert _call(good, 16, 8, 1, 2, good + 2, good) == e["MXQ_E_ALIGN"]
     assert _call(good, 16, 8, 1, 1, good, good + 1) == e["MXQ_E_ALIGN"]
+
+
+def _dq(d, s, P, F, fmt, res, out):
+    return mxq.load().mxq_dequantize(d, s, P, F, fmt, res, out, None)
+
+
+def test_dequantize_validation_errors_before_launch():
+    e = _header_enums()
+    good = 4096
+    assert _dq(good, good, 16, 8, 3, 0, good) == e["MXQ_E_OUT_DTYPE"]
+    assert _dq(good, good, 16, 8, 0, 2, good) == e["MXQ_E_RES_DTYPE"]
+    assert _dq(good, good, 12, 8, 0, 0, good) == e["MXQ_E_SHAPE_P8"]
+    assert _dq(good, good, 16, 6, 0, 0, good) == e["MXQ_E_SHAPE_F4"]
+    assert _dq(good, good, 1 << 40, 1 << 22, 0, 0, good) == e["MXQ_E_OVERFLOW"]
+    assert _dq(None, good, 16, 8, 0, 0, good) == e["MXQ_E_NULL"]
+    assert _dq(good, None, 16, 8, 0, 1, good) == e["MXQ_E_NULL"]
+    assert _dq(good, good, 16, 8, 2, 1, None) == e["MXQ_E_NULL"]
+    assert _dq(good + 4, good, 16, 8, 0, 0, good) == e["MXQ_E_ALIGN"]
+    assert _dq(good, good + 2, 16, 8, 0, 0, good) == e["MXQ_E_ALIGN"]
+    assert _dq(good, good, 16, 8, 0, 0, good + 8) == e["MXQ_E_ALIGN"]
+    for P, F in ((0, 8), (8, 0)):
+        assert _dq(None, None, P, F, 0, 0, None) == 0
+
+
+def test_result_bytes():
+    import torch
+
+    assert mxq.result_bytes(16, 8, torch.float32) == 512
+    assert mxq.result_bytes(16, 8, torch.bfloat16) == 256
+    assert mxq.load().mxq_result_bytes(16, 8, 5) == 0
+    assert mxq.load().mxq_result_bytes(12, 8, 0) == 0
 
 
 def test_empty_tensors_are_noops():

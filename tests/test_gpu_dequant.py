@@ -1,0 +1,109 @@
+"""GPU parity of the MX dequantize against the CPU oracle.
+
+Results are compared bit for bit; where the result is a NaN only its
+position is compared (the payload of a NaN is not unique). Every case also
+checks that nothing is written past the end of the result buffer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_microscaling_quantization_amd as mxq
+import oracle
+import workloads
+from conftest import progress
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ("e4m3fn", "e5m2", "e2m1")
+RES = {"f32": torch.float32, "bf16": torch.bfloat16}
+GUARD = 64
+
+
+def _np_view(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().view(np.uint32)
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, fmt: str, res: str) -> np.ndarray:
+    d = torch.from_numpy(np.ascontiguousarray(data).reshape(mxq.data_shape(P, F, fmt))).cuda()
+    im = torch.from_numpy(np.ascontiguousarray(image)).cuda()
+    buf = torch.full((P * F + GUARD,), 7.0, dtype=RES[res], device="cuda")
+    out = buf[: P * F].view(P, F)
+    mxq.dequantize(d, im, fmt, RES[res], out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[P * F:] == 7.0).all()), "write past the end of the result buffer"
+    return _np_view(out)
+
+
+def assert_same(got: np.ndarray, ref: np.ndarray, res: str, tag: str):
+    ref_bits = ref.view(np.uint32) if res == "f32" else ref
+    if res == "f32":
+        nan_g = (got & 0x7FFFFFFF) > 0x7F800000
+        nan_r = (ref_bits & 0x7FFFFFFF) > 0x7F800000
+    else:
+        nan_g = (got & 0x7FFF) > 0x7F80
+        nan_r = (ref_bits & 0x7FFF) > 0x7F80
+    assert np.array_equal(nan_g, nan_r), "%s: NaN positions differ" % tag
+    ok = got[~nan_g] == ref_bits[~nan_r]
+    if not ok.all():
+        idx = np.argwhere(~nan_g)[~ok][0]
+        raise AssertionError("%s: %d results differ, first at %s: gpu %#x oracle %#x"
+                             % (tag, int((~ok).sum()), tuple(idx), got[tuple(idx)], ref_bits[tuple(idx)]))
+
+
+def _data_bytes(P, F, fmt):
+    return P * F // 2 if fmt == "e2m1" else P * F
+
+
+@pytest.mark.parametrize("res", list(RES))
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("P,F", [(8, 4), (16, 12), (40, 8), (64, 96), (264, 1032), (136, 2052), (32, 8192)])
+def test_random_codes_and_scales(fmt, res, P, F):
+    """Every code, including NaN/Inf codes, under random E8M0 bytes
+    (0 and 255 included)."""
+    progress("dequant random %s->%s %dx%d" % (fmt, res, P, F))
+    rng = np.random.default_rng(P * 1009 + F)
+    data = rng.integers(0, 256, size=_data_bytes(P, F, fmt), dtype=np.uint8)
+    image = rng.integers(0, 256, size=(P, F // 4), dtype=np.uint8)
+    image[0] = np.resize(np.array([0, 255, 254, 1, 127], np.uint8), image.shape[1])
+    got = gpu_dequantize(data, image, P, F, fmt, res)
+    ref = oracle.dequantize(data, image, P, F, fmt, res).reshape(P, F)
+    assert_same(got, ref, res, "random")
+
+
+@pytest.mark.parametrize("res", list(RES))
+@pytest.mark.parametrize("in_dtype,fmt", [(i, f) for i in ("bf16", "f16") for f in FMTS])
+def test_roundtrip_after_gpu_quantize(in_dtype, fmt, res):
+    P, F = 264, 1032
+    x = workloads.random_bits(P, F, in_dtype, seed=77, specials=True)
+    tdt = torch.bfloat16 if in_dtype == "bf16" else torch.float16
+    xt = torch.from_numpy(x.view(np.int16)).view(tdt).cuda()
+    d, im = mxq.quantize(xt, fmt)
+    out = mxq.dequantize(d, im, fmt, RES[res])
+    torch.cuda.synchronize()
+    d_ref, im_ref = oracle.quantize(x, in_dtype, fmt, image=im.cpu().numpy())
+    assert np.array_equal(d.cpu().numpy(), d_ref)
+    ref = oracle.dequantize(d_ref, im_ref, P, F, fmt, res).reshape(P, F)
+    assert_same(_np_view(out), ref, res, "roundtrip")
+
+
+def test_full_size_dequantize_sampled():
+    """Dequantize of the 1.07 G-element e4m3fn tensor to bf16 (the bench's
+    dequantize call); the oracle checks 32 sampled 32-row slabs."""
+    P, F = 131072, 8192
+    progress("dequant full size: generate + quantize")
+    xt = workloads.colscaled_bf16_device(P, F, seed=5)
+    d, im = mxq.quantize(xt, "e4m3fn")
+    del xt
+    progress("dequant full size: dequantize")
+    out = mxq.dequantize(d, im, "e4m3fn", torch.bfloat16)
+    torch.cuda.synchronize()
+    progress("dequant full size: sampled oracle check")
+    rng = np.random.default_rng(56)
+    for q in np.unique(np.concatenate([[0, P // 32 - 1], rng.integers(0, P // 32, size=30)])):
+        rows = slice(32 * int(q), 32 * int(q) + 32)
+        ref = oracle.dequantize(d[rows].cpu().numpy(), im[rows].cpu().numpy(), 32, F, "e4m3fn", "bf16")
+        assert_same(_np_view(out[rows]), ref.reshape(32, F), "bf16", "slab %d" % q)
+    assert not bool(torch.isnan(out).any()) and not bool(torch.isinf(out).any())
