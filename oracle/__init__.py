@@ -51,9 +51,11 @@ def _load():
         c = ctypes
         P_u16, P_u8, P_f32, P_f64 = (c.POINTER(c.c_uint16), c.POINTER(c.c_uint8),
                                       c.POINTER(c.c_float), c.POINTER(c.c_double))
-        lib.mxq_oracle_quantize.argtypes = [P_u16, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int, P_u8, P_u8]
+        lib.mxq_oracle_quantize.argtypes = [P_u16, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int,
+                                            P_u8, P_u8]
         lib.mxq_oracle_quantize.restype = c.c_int
-        lib.mxq_oracle_dequantize.argtypes = [P_u8, P_u8, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_void_p]
+        lib.mxq_oracle_dequantize.argtypes = [P_u8, P_u8, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int,
+                                              c.c_void_p]
         lib.mxq_oracle_dequantize.restype = c.c_int
         lib.mxq_oracle_f32_to_bf16_array.argtypes = [P_f32, c.c_int64, P_u16]
         lib.mxq_oracle_widen_array.argtypes = [P_u16, c.c_int64, c.c_int, P_f32]
@@ -86,25 +88,34 @@ def data_shape(P: int, F: int, out_dtype: str):
     return (P, F // 2) if out_dtype == "e2m1" else (P, F)
 
 
+LAYOUTS = {"image": 0, "dense": 1}
+
+
+def scale_shape(P: int, F: int, layout: str = "image"):
+    return (P, F // 4) if layout == "image" else (P // 8, F // 4)
+
+
 def quantize(x: np.ndarray, in_dtype: str, out_dtype: str, alt_emax: bool = False,
-             image: np.ndarray | None = None):
+             image: np.ndarray | None = None, layout: str = "image"):
     """Quantize a [P, F] array of bf16/f16 bit patterns (uint16).
 
     Returns ``(data, image)``: data is uint8 [P, F] (FP8) or [P, F/2] (FP4);
-    image is the uint8 [P, F/4] scale image. Only the rows that the scale
-    placement names are written; the others keep the contents of ``image``
-    (zeros when it is not given).
+    image is the uint8 [P, F/4] scale image, of which only the rows that the
+    scale placement names are written (the others keep the contents of
+    ``image``, zeros when it is not given); with ``layout="dense"`` it is the
+    fully written [P/8, F/4] scale array.
     """
     lib = _load()
     x = np.ascontiguousarray(x, dtype=np.uint16)
     P, F = x.shape
     data = np.zeros(data_shape(P, F, out_dtype), dtype=np.uint8)
     if image is None:
-        image = np.zeros((P, F // 4), dtype=np.uint8)
+        image = np.zeros(scale_shape(P, F, layout), dtype=np.uint8)
     else:
         image = np.array(image, dtype=np.uint8, copy=True, order="C")
     rc = lib.mxq_oracle_quantize(_ptr(x, ctypes.c_uint16), P, F, IN_CODES[in_dtype], OUT_CODES[out_dtype],
-                                 int(bool(alt_emax)), _ptr(data, ctypes.c_uint8), _ptr(image, ctypes.c_uint8))
+                                 int(bool(alt_emax)), LAYOUTS[layout], _ptr(data, ctypes.c_uint8),
+                                 _ptr(image, ctypes.c_uint8))
     if rc != 0:
         raise ValueError("oracle quantize rejected the call (status %d)" % rc)
     return data, image
@@ -114,15 +125,16 @@ RES_CODES = {"f32": 0, "bf16": 1}
 
 
 def dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, out_dtype: str,
-               res_dtype: str = "f32") -> np.ndarray:
-    """Decode [P, F] values from packed data and the scale image: float32, or
-    bf16 bit patterns (uint16) for ``res_dtype="bf16"``."""
+               res_dtype: str = "f32", layout: str = "image") -> np.ndarray:
+    """Decode [P, F] values from packed data and the scale image (or dense
+    scale array): float32, or bf16 bit patterns (uint16) for
+    ``res_dtype="bf16"``."""
     lib = _load()
     data = np.ascontiguousarray(data, dtype=np.uint8)
     image = np.ascontiguousarray(image, dtype=np.uint8)
     out = np.empty((P, F), dtype=np.float32 if res_dtype == "f32" else np.uint16)
     rc = lib.mxq_oracle_dequantize(_ptr(data, ctypes.c_uint8), _ptr(image, ctypes.c_uint8), P, F,
-                                   OUT_CODES[out_dtype], RES_CODES[res_dtype], out.ctypes.data)
+                                   OUT_CODES[out_dtype], RES_CODES[res_dtype], LAYOUTS[layout], out.ctypes.data)
     if rc != 0:
         raise ValueError("oracle dequantize rejected the call (status %d)" % rc)
     return out

@@ -38,6 +38,7 @@
 #define ORC_BAD_P 3
 #define ORC_BAD_F 4
 #define ORC_NO_MEMORY 5
+#define ORC_BAD_LAYOUT 6
 
 static uint32_t bits_of(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 static float float_of(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
@@ -135,6 +136,13 @@ uint8_t mxq_oracle_e8m0(uint8_t max_exponent, int emax_bias)
 float mxq_oracle_prescale(float x, uint8_t e8m0)
 {
     float multiplier = float_of((uint32_t)(254 - (int)e8m0) << 23);
+    /* reading: E8M0 254 (reachable only with the alternative EMAX bias and
+     * FP4, for a block holding Inf or NaN) makes the multiplier +0. The page
+     * asserts this never happens; IEEE leaves the sign of the NaN that
+     * Inf * 0 produces open, so it is fixed here to the Inf's own sign
+     * instead of inheriting the host CPU's default NaN. */
+    if (multiplier == 0.0f && isinf(x))
+        return copysignf(NAN, x);
     return multiplier * x;
 }
 
@@ -316,15 +324,26 @@ static void pack_nibble(uint8_t *base, int64_t index, uint8_t nibble)
 
 /* ------------------------------------------------------------------------
  * Step 7 -- scale placement.
+ * Layouts: ORC_SCALE_IMAGE (the placement below, the default) or
+ * ORC_SCALE_DENSE (plain row-major [P/8, F/4], the layout the page also
+ * gives as the scale tensor's shape; offered as a variant).
  * [NUM] "x4-Pack and Scale-Tensor Interleave", E8M0 Scale-Tensor Layout:
  * logical scale row i (i < P/8, F/4 bytes) is copied to output row
  * (i mod 4) + 32 * floor(i / 4).
  * reading: the scale output is an image of P rows of F/4 bytes; only the
  * rows named by that formula are written, the rest are left untouched.
  * ---------------------------------------------------------------------- */
+#define ORC_SCALE_IMAGE 0
+#define ORC_SCALE_DENSE 1
+
 int64_t mxq_oracle_scale_slot(int64_t i)
 {
     return (i & 3) + 32 * (i >> 2);
+}
+
+static int64_t scale_row(int64_t i, int layout)
+{
+    return layout == ORC_SCALE_DENSE ? i : mxq_oracle_scale_slot(i);
 }
 
 /* ------------------------------------------------------------------------
@@ -338,12 +357,13 @@ int64_t mxq_oracle_scale_slot(int64_t i)
  *              FP4: P*F/2 bytes, nibbles placed by pack_nibble over the
  *              row-major element index.
  * scale_image: P rows of F/4 bytes; rows not named by the placement formula
- *              are not written.
+ *              are not written. With scale_layout ORC_SCALE_DENSE: P/8 rows
+ *              of F/4 bytes, all written.
  * alt_emax:    0 = EMAX bias (the default mode), 1 = EMAX - 1.
  * Returns ORC_OK or an ORC_* error; on error nothing is written.
  * ---------------------------------------------------------------------- */
 int mxq_oracle_quantize(const uint16_t *in, int64_t P, int64_t F, int in_dtype, int out_dtype,
-                        int alt_emax, uint8_t *data_out, uint8_t *scale_image)
+                        int alt_emax, int scale_layout, uint8_t *data_out, uint8_t *scale_image)
 {
     if (in_dtype != ORC_IN_BF16 && in_dtype != ORC_IN_F16)
         return ORC_BAD_IN_DTYPE;
@@ -354,6 +374,8 @@ int mxq_oracle_quantize(const uint16_t *in, int64_t P, int64_t F, int in_dtype, 
         return ORC_BAD_P;
     if (F < 0 || F % 4 != 0)
         return ORC_BAD_F;
+    if (scale_layout != ORC_SCALE_IMAGE && scale_layout != ORC_SCALE_DENSE)
+        return ORC_BAD_LAYOUT;
     if (P == 0 || F == 0)
         return ORC_OK;
 
@@ -396,7 +418,7 @@ int mxq_oracle_quantize(const uint16_t *in, int64_t P, int64_t F, int in_dtype, 
 
     /* 7. place the logical scale rows */
     for (int64_t i = 0; i < groups; i++)
-        memcpy(scale_image + mxq_oracle_scale_slot(i) * blocks, scale2d + i * blocks, (size_t)blocks);
+        memcpy(scale_image + scale_row(i, scale_layout) * blocks, scale2d + i * blocks, (size_t)blocks);
 
     free(x);
     free(y);
@@ -444,21 +466,23 @@ static uint8_t unpack_code(const uint8_t *data, int64_t k, int out_dtype)
 }
 
 /* out: P x F results, row-major: float (ORC_RES_F32) or bf16 bit patterns
- * (ORC_RES_BF16). */
+ * (ORC_RES_BF16). scale_layout as for mxq_oracle_quantize. */
 int mxq_oracle_dequantize(const uint8_t *data, const uint8_t *scale_image, int64_t P, int64_t F,
-                          int out_dtype, int res_dtype, void *out)
+                          int out_dtype, int res_dtype, int scale_layout, void *out)
 {
     if (mxq_oracle_emax(out_dtype) < 0)
         return ORC_BAD_OUT_DTYPE;
     if (res_dtype != ORC_RES_F32 && res_dtype != ORC_RES_BF16)
         return ORC_BAD_IN_DTYPE;
+    if (scale_layout != ORC_SCALE_IMAGE && scale_layout != ORC_SCALE_DENSE)
+        return ORC_BAD_LAYOUT;
     if (P < 0 || P % 8 != 0)
         return ORC_BAD_P;
     if (F < 0 || F % 4 != 0)
         return ORC_BAD_F;
     int64_t blocks = F / 4;
     for (int64_t p = 0; p < P; p++) {
-        const uint8_t *srow = scale_image + mxq_oracle_scale_slot(p / 8) * blocks;
+        const uint8_t *srow = scale_image + scale_row(p / 8, scale_layout) * blocks;
         for (int64_t f = 0; f < F; f++) {
             int64_t k = p * F + f;
             double v = mxq_oracle_decode(unpack_code(data, k, out_dtype), out_dtype);

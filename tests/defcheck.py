@@ -112,8 +112,10 @@ def scale_slot(i: np.ndarray) -> np.ndarray:
     return (i % 4) + 32 * (i // 4)
 
 
-def quantize(x: np.ndarray, in_dtype: str, fmt: str, alt: bool = False, image: np.ndarray | None = None):
-    """Whole quantize by the definitions above; returns (data, image)."""
+def quantize(x: np.ndarray, in_dtype: str, fmt: str, alt: bool = False, image: np.ndarray | None = None,
+             layout: str = "image"):
+    """Whole quantize by the definitions above; returns (data, image).
+    layout "dense" returns the [P/8, F/4] scale array instead of the image."""
     x = np.asarray(x, dtype=np.uint16)
     P, F = x.shape
     v = widen(x, in_dtype)
@@ -122,6 +124,9 @@ def quantize(x: np.ndarray, in_dtype: str, fmt: str, alt: bool = False, image: n
     e = e8m0_closed_form(absmax, fmt, alt)             # [P/8, F/4]
     e_full = np.repeat(np.repeat(e, 8, axis=0), 4, axis=1).astype(np.int64)
     y = v * np.ldexp(1.0, 127 - e_full)                # exact in float64
+    # reading: E8M0 254 (alternative bias, FP4, non-finite block) has a zero
+    # multiplier, so every element of such a block is a zero of its own sign
+    y = np.where(e_full == 254, np.copysign(0.0, v), y)
     codes = narrow_bruteforce(y, fmt).reshape(P, F)
     if fmt == "e2m1":
         tab = container_table()
@@ -133,6 +138,8 @@ def quantize(x: np.ndarray, in_dtype: str, fmt: str, alt: bool = False, image: n
             out[:, :, byte] |= (c4[:, :, k] << (4 if hi else 0)).astype(np.uint8)
     else:
         data = codes.astype(np.uint8)
+    if layout == "dense":
+        return data, e.astype(np.uint8)
     if image is None:
         image = np.zeros((P, F // 4), dtype=np.uint8)
     else:

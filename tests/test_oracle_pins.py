@@ -266,12 +266,56 @@ def test_oracle_equals_definitions_tiny(in_dtype, fmt, P, F):
         assert np.array_equal(im_or, im_df)
 
 
+@pytest.mark.parametrize("in_dtype", INS)
 @pytest.mark.parametrize("fmt", FMTS)
-def test_oracle_equals_definitions_alt_emax(fmt):
-    x = workloads.random_bits(64, 64, "bf16", seed=31)           # finite inputs
-    d_or, im_or = oracle.quantize(x, "bf16", fmt, alt_emax=True)
-    d_df, im_df = defcheck.quantize(x, "bf16", fmt, alt=True)
-    assert np.array_equal(d_or, d_df) and np.array_equal(im_or, im_df)
+@pytest.mark.parametrize("layout", ("image", "dense"))
+@pytest.mark.parametrize("alt", (False, True))
+def test_oracle_equals_definitions_modes(in_dtype, fmt, layout, alt):
+    for seed in range(3):
+        x = workloads.random_bits(64, 36, in_dtype, seed=31 + seed, specials=True)
+        d_or, im_or = oracle.quantize(x, in_dtype, fmt, alt_emax=alt, layout=layout)
+        d_df, im_df = defcheck.quantize(x, in_dtype, fmt, alt=alt, layout=layout)
+        assert np.array_equal(d_or, d_df) and np.array_equal(im_or, im_df)
+
+
+def test_alt_emax_page_values_and_worked_example():
+    # alternative mode: bias EMAX - 1 (7 for e4m3fn, 14 for e5m2)
+    c = _golden_constants()
+    for fmt in ("e4m3fn", "e5m2"):
+        assert oracle.emax(fmt) - 1 == int(c["emax_alt." + fmt])
+    # one block, max 256 (biased exponent 135): E8M0 135 - 7 = 128, multiplier
+    # 2^-1, so 256 -> 128 = e4m3fn exponent field 14, mantissa 0 -> 0x70
+    x = np.zeros((8, 4), np.uint16)
+    x[0, 0] = workloads.f32_to_bf16_bits(np.array([256.0], np.float32))[0]
+    data, image = oracle.quantize(x, "bf16", "e4m3fn", alt_emax=True)
+    assert image[0, 0] == 128 and data[0, 0] == 0x70
+    data, image = oracle.quantize(x, "bf16", "e4m3fn")
+    assert image[0, 0] == 127 and data[0, 0] == 0x78
+
+
+def test_alt_emax_fp4_nonfinite_block_reading():
+    """E8M0 254: the page's multiplier is +0; every element of the block
+    becomes a zero of its own sign (Inf * 0 read as a NaN of the Inf's sign)."""
+    x = workloads.f32_to_bf16_bits(np.linspace(-3, 3, 32, dtype=np.float32)).reshape(8, 4)
+    x[0, 0], x[0, 1], x[0, 2] = 0x7F80, 0xFF80, 0xFFC0      # +Inf, -Inf, -NaN
+    data, image = oracle.quantize(x, "bf16", "e2m1", alt_emax=True)
+    assert image[0, 0] == 254
+    codes = defcheck.unpack_codes(data, 8, 4, "e2m1")
+    signs = (x >> 15).astype(np.uint8)
+    assert np.array_equal(codes, signs << 3)
+
+
+def test_dense_layout_is_the_placed_rows():
+    x = workloads.random_bits(256, 64, "f16", seed=33, specials=True)
+    for fmt in FMTS:
+        d_img, im = oracle.quantize(x, "f16", fmt)
+        d_den, dense = oracle.quantize(x, "f16", fmt, layout="dense")
+        assert np.array_equal(d_img, d_den)
+        assert np.array_equal(dense, im[defcheck.scale_slot(np.arange(32))])
+        for res in ("f32", "bf16"):
+            a = oracle.dequantize(d_img, im, 256, 64, fmt, res)
+            b = oracle.dequantize(d_den, dense, 256, 64, fmt, res, layout="dense")
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 # -------------------------------------------------------------- properties
