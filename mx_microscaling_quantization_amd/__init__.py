@@ -27,6 +27,8 @@ _LIB_NAME = "libmxq.so"
 IN_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
 OUT_DTYPES = {"e4m3fn": 0, "e5m2": 1, "e2m1": 2}
 RES_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+FLAG_ALT_EMAX = 1
+FLAG_DENSE_SCALE = 2
 ABI_VERSION = 1
 
 _lock = threading.Lock()
@@ -59,6 +61,14 @@ def load():
         lib.mxq_quantize.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_void_p,
                                      c.c_void_p, c.c_void_p]
         lib.mxq_quantize.restype = c.c_int
+        lib.mxq_quantize_ex.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_uint,
+                                        c.c_void_p, c.c_void_p, c.c_void_p]
+        lib.mxq_quantize_ex.restype = c.c_int
+        lib.mxq_dequantize_ex.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int,
+                                          c.c_uint, c.c_void_p, c.c_void_p]
+        lib.mxq_dequantize_ex.restype = c.c_int
+        lib.mxq_scale_bytes.argtypes = [c.c_int64, c.c_int64, c.c_uint]
+        lib.mxq_scale_bytes.restype = c.c_size_t
         lib.mxq_data_bytes.argtypes = [c.c_int64, c.c_int64, c.c_int]
         lib.mxq_data_bytes.restype = c.c_size_t
         lib.mxq_scale_image_bytes.argtypes = [c.c_int64, c.c_int64]
@@ -111,8 +121,10 @@ def data_shape(P: int, F: int, out_dtype: str):
     return (P, F // 2) if out_dtype == "e2m1" else (P, F)
 
 
-def scale_image_shape(P: int, F: int):
-    return (P, F // 4)
+def scale_image_shape(P: int, F: int, dense_scale: bool = False):
+    """uint8 shape of the scale output: the [P, F/4] image, or [P/8, F/4]
+    with ``dense_scale``."""
+    return (P // 8, F // 4) if dense_scale else (P, F // 4)
 
 
 def logical_scale_view(image: torch.Tensor) -> torch.Tensor:
@@ -125,14 +137,17 @@ def logical_scale_view(image: torch.Tensor) -> torch.Tensor:
 
 
 def quantize(x: torch.Tensor, out_dtype: str = "e4m3fn", data_out: torch.Tensor | None = None,
-             scale_out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+             scale_out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
+             alt_emax: bool = False, dense_scale: bool = False):
     """MX-quantize a contiguous [P, F] bf16/f16 CUDA (HIP) tensor.
 
-    Returns ``(data, scale_image)`` as uint8 tensors: data [P, F] (FP8) or
+    Returns ``(data, scale)`` as uint8 tensors: data [P, F] (FP8) or
     [P, F/2] (FP4); the scale image [P, F/4], of which rows
     (i mod 4) + 32 * floor(i / 4) hold row group i's E8M0 bytes and the other
-    rows keep whatever ``scale_out`` held. The kernel is enqueued on
-    ``stream`` (default: the current stream of x's device).
+    rows keep whatever ``scale_out`` held -- or, with ``dense_scale``, the
+    dense [P/8, F/4] scale array. ``alt_emax`` selects the EMAX - 1 bias.
+    The kernel is enqueued on ``stream`` (default: the current stream of x's
+    device).
     """
     lib = load()
     if x.dtype not in IN_DTYPES:
@@ -147,29 +162,31 @@ def quantize(x: torch.Tensor, out_dtype: str = "e4m3fn", data_out: torch.Tensor 
     P, F = x.shape
     if data_out is None:
         data_out = torch.empty(data_shape(P, F, out_dtype), dtype=torch.uint8, device=x.device)
+    flags = (FLAG_ALT_EMAX if alt_emax else 0) | (FLAG_DENSE_SCALE if dense_scale else 0)
     if scale_out is None:
-        scale_out = torch.empty(scale_image_shape(P, F), dtype=torch.uint8, device=x.device)
+        scale_out = torch.empty(scale_image_shape(P, F, dense_scale), dtype=torch.uint8, device=x.device)
     for name, t, nbytes in (("data_out", data_out, lib.mxq_data_bytes(P, F, code)),
-                            ("scale_out", scale_out, lib.mxq_scale_image_bytes(P, F))):
+                            ("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags))):
         if t.device != x.device or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
             raise ValueError("%s must be a contiguous buffer of >= %d bytes on %s" % (name, nbytes, x.device))
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
-        _check(lib.mxq_quantize(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, data_out.data_ptr(),
-                                scale_out.data_ptr(), stream.cuda_stream))
+        _check(lib.mxq_quantize_ex(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, flags, data_out.data_ptr(),
+                                   scale_out.data_ptr(), stream.cuda_stream))
     return data_out, scale_out
 
 
 def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "e4m3fn",
                res_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
-               stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+               stream: torch.cuda.Stream | None = None, dense_scale: bool = False) -> torch.Tensor:
     """Decode MX data back to [P, F] float32 or bfloat16.
 
     ``data`` is the uint8 data output of :func:`quantize` for format
     ``out_dtype`` ([P, F] FP8 or [P, F/2] FP4) and ``scale_image`` its
-    [P, F/4] scale image. Each result is decode(code) * 2^(E8M0 - 127),
-    rounded once to float32 (then nearest-even to bfloat16).
+    [P, F/4] scale image (or, with ``dense_scale``, its [P/8, F/4] scale
+    array). Each result is decode(code) * 2^(E8M0 - 127), rounded once to
+    float32 (then nearest-even to bfloat16).
     """
     lib = load()
     code = _out_code(out_dtype)
@@ -183,7 +200,8 @@ def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "
         raise ValueError("data and scale_image must be contiguous")
     P = data.shape[0]
     F = scale_image.shape[1] * 4
-    if tuple(data.shape) != data_shape(P, F, out_dtype) or tuple(scale_image.shape) != scale_image_shape(P, F):
+    if tuple(data.shape) != data_shape(P, F, out_dtype) or \
+            tuple(scale_image.shape) != scale_image_shape(P, F, dense_scale):
         raise ValueError("data %s / scale_image %s do not describe one [P, F] tensor in format %s"
                          % (tuple(data.shape), tuple(scale_image.shape), out_dtype))
     if out is None:
@@ -193,6 +211,6 @@ def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "
     if stream is None:
         stream = torch.cuda.current_stream(data.device)
     with torch.cuda.device(data.device):
-        _check(lib.mxq_dequantize(data.data_ptr(), scale_image.data_ptr(), P, F, code, RES_DTYPES[res_dtype],
-                                  out.data_ptr(), stream.cuda_stream))
+        _check(lib.mxq_dequantize_ex(data.data_ptr(), scale_image.data_ptr(), P, F, code, RES_DTYPES[res_dtype],
+                                     FLAG_DENSE_SCALE if dense_scale else 0, out.data_ptr(), stream.cuda_stream))
     return out

@@ -22,7 +22,8 @@ constexpr uint32_t kThreads = 64;
 constexpr int64_t kMaxF = (int64_t)1 << 31;
 constexpr int64_t kMaxWorkgroups = ((int64_t)1 << 31) - 1;
 
-typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, uint32_t);
+typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, uint32_t, int,
+                          uint32_t);
 
 // Row groups per thread, and non-temporal loads and stores (bit 0 | bit 1):
 // every byte is touched exactly once, so nothing is worth keeping in cache.
@@ -44,7 +45,7 @@ template <int IN> kernel_fn pick_out(int out_dtype, int nb)
     }
 }
 
-typedef void (*dq_kernel_fn)(const uint8_t *, const uint8_t *, void *, uint64_t, uint32_t, uint32_t);
+typedef void (*dq_kernel_fn)(const uint8_t *, const uint8_t *, void *, uint64_t, uint32_t, uint32_t, uint32_t);
 
 template <int FMT, int RES> dq_kernel_fn dq_pick_nb(int nb)
 {
@@ -58,6 +59,17 @@ template <int RES> dq_kernel_fn dq_pick_fmt(int fmt, int nb)
     case MXQ_OUT_E4M3FN: return dq_pick_nb<mxq::kOutE4M3FN, RES>(nb);
     case MXQ_OUT_E5M2: return dq_pick_nb<mxq::kOutE5M2, RES>(nb);
     default: return dq_pick_nb<mxq::kOutE2M1, RES>(nb);
+    }
+}
+
+// Largest normal exponent of each output format ("Block-Scale Computation",
+// The EMAX Table): the bias subtracted from a block's maximum exponent.
+int emax_of(int out_dtype)
+{
+    switch (out_dtype) {
+    case MXQ_OUT_E4M3FN: return 8;
+    case MXQ_OUT_E5M2: return 15;
+    default: return 2;
     }
 }
 
@@ -117,6 +129,13 @@ size_t mxq_scale_image_bytes(int64_t P, int64_t F)
     return (size_t)(P * (F / 4));
 }
 
+size_t mxq_scale_bytes(int64_t P, int64_t F, unsigned flags)
+{
+    if (check_shape(P, F) != MXQ_OK || (flags & ~(unsigned)(MXQ_FLAG_ALT_EMAX | MXQ_FLAG_DENSE_SCALE)))
+        return 0;
+    return (size_t)((flags & MXQ_FLAG_DENSE_SCALE) ? (P / 8) * (F / 4) : P * (F / 4));
+}
+
 size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype)
 {
     if (check_shape(P, F) != MXQ_OK)
@@ -131,10 +150,18 @@ size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype)
 int mxq_dequantize(const void *data, const void *scale_in, int64_t P, int64_t F, int fmt, int res_dtype,
                    void *out, void *stream)
 {
+    return mxq_dequantize_ex(data, scale_in, P, F, fmt, res_dtype, 0u, out, stream);
+}
+
+int mxq_dequantize_ex(const void *data, const void *scale_in, int64_t P, int64_t F, int fmt, int res_dtype,
+                      unsigned flags, void *out, void *stream)
+{
     if (fmt != MXQ_OUT_E4M3FN && fmt != MXQ_OUT_E5M2 && fmt != MXQ_OUT_E2M1)
         return MXQ_E_OUT_DTYPE;
     if (res_dtype != MXQ_RES_F32 && res_dtype != MXQ_RES_BF16)
         return MXQ_E_RES_DTYPE;
+    if (flags & ~(unsigned)MXQ_FLAG_DENSE_SCALE)
+        return MXQ_E_FLAGS;
     int rc = check_shape(P, F);
     if (rc != MXQ_OK)
         return rc;
@@ -162,7 +189,8 @@ int mxq_dequantize(const void *data, const void *scale_in, int64_t P, int64_t F,
     uint64_t a3 = (uint64_t)F;
     uint32_t a4 = (uint32_t)nstrips;
     uint32_t a5 = (uint32_t)tiles_per_group;
-    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5};
+    uint32_t a6 = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
+    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6};
     hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(groups * tiles_per_group)), dim3(kThreads),
                                      args, 0, (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
@@ -171,10 +199,18 @@ int mxq_dequantize(const void *data, const void *scale_in, int64_t P, int64_t F,
 int mxq_quantize(const void *in, int64_t P, int64_t F, int in_dtype, int out_dtype, void *data_out,
                  void *scale_out, void *stream)
 {
+    return mxq_quantize_ex(in, P, F, in_dtype, out_dtype, 0u, data_out, scale_out, stream);
+}
+
+int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_dtype, unsigned flags,
+                    void *data_out, void *scale_out, void *stream)
+{
     if (in_dtype != MXQ_IN_BF16 && in_dtype != MXQ_IN_F16)
         return MXQ_E_IN_DTYPE;
     if (out_dtype != MXQ_OUT_E4M3FN && out_dtype != MXQ_OUT_E5M2 && out_dtype != MXQ_OUT_E2M1)
         return MXQ_E_OUT_DTYPE;
+    if (flags & ~(unsigned)(MXQ_FLAG_ALT_EMAX | MXQ_FLAG_DENSE_SCALE))
+        return MXQ_E_FLAGS;
     int rc = check_shape(P, F);
     if (rc != MXQ_OK)
         return rc;
@@ -203,7 +239,9 @@ int mxq_quantize(const void *in, int64_t P, int64_t F, int in_dtype, int out_dty
     uint32_t a4 = (uint32_t)nstrips;
     uint32_t a5 = (uint32_t)tiles_per_band;
     uint32_t a6 = (uint32_t)groups;
-    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6};
+    int a7 = emax_of(out_dtype) - ((flags & MXQ_FLAG_ALT_EMAX) ? 1 : 0);
+    uint32_t a8 = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
+    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7, &a8};
     hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(bands * tiles_per_band)), dim3(threads),
                                      args, 0, (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;

@@ -112,13 +112,15 @@ __device__ __forceinline__ void decode_block_e255(uint32_t w, uint32_t *out)
 // The dequantize kernel. Grid as the quantize (GPT = 1): one workgroup per
 // (row group, run of blockDim.x strips).
 //   data    FP8: P*F bytes; FP4: P*F/2 bytes
-//   scale   the P x F/4 scale image (only the placed rows are read)
+//   scale   the P x F/4 scale image (only the placed rows are read), or with
+//           dense = 1 the [P/8, F/4] scale array
 //   out     P x F results, fp32 or bf16
 template <int FMT, int RES, int NB, int NT>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restrict__ data,
                                                          const uint8_t *__restrict__ scale,
                                                          void *__restrict__ out, uint64_t F,
-                                                         uint32_t nstrips, uint32_t tiles_per_band)
+                                                         uint32_t nstrips, uint32_t tiles_per_band,
+                                                         uint32_t dense)
 {
     static_assert(NB == 1 || NB == 2, "a strip is 1 or 2 blocks");
     constexpr int LD = NT & 1, ST = (NT >> 1) & 1;
@@ -129,7 +131,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
         return;
 
     // the strip's E8M0 bytes, from logical row `group`'s placed image row
-    const uint64_t slot = (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
+    // (or its row of the dense array)
+    const uint64_t slot = dense ? (uint64_t)group : (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
     const uint8_t *srow = scale + slot * (F / 4) + (uint64_t)strip * NB;
     uint32_t e[NB];
     if constexpr (NB == 2) {

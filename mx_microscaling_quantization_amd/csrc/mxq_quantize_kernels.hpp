@@ -18,7 +18,8 @@
 //    monotone in |x|; so the kernel takes a packed 16-bit max over the
 //    magnitude bits (v_pk_max_u16) and widens only that one value
 //    (findMaxExponentPerInputBlock);
-//  * E8M0 = max(1, m - EMAX) (generateMxScales, both clamps at once);
+//  * E8M0 = max(1, m - bias) (generateMxScales, both clamps at once), with
+//    bias = EMAX, or EMAX - 1 in the alternative mode;
 //  * prescale + round + pack run on gfx950's scaled conversions
 //    (v_cvt_scalef32_pk_{fp8,bf8,fp4}_{bf16,f16}), which compute
 //    RNE(x / scale) from the 16-bit inputs directly. With scale =
@@ -33,7 +34,10 @@
 //  * NaN inputs: the conversions give a NaN code (FP8) or +-6 (FP4), while
 //    the quantizer's rule is a zero with the NaN's sign. A NaN can only sit
 //    in a block whose maximum magnitude pattern is above the Inf pattern, so
-//    a rarely taken per-thread branch rewrites exactly those codes.
+//    a rarely taken per-thread branch rewrites exactly those codes;
+//  * E8M0 254 (only FP4 in the alternative mode, for a block holding Inf or
+//    NaN) makes the page's multiplier +0: every element of such a block is a
+//    zero of its own sign. The same branch writes those codes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,12 +52,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-
-// Largest normal exponent of each output format (the EMAX table).
-template <int OUT> struct Emax;
-template <> struct Emax<kOutE4M3FN> { static constexpr int value = 8; };
-template <> struct Emax<kOutE5M2> { static constexpr int value = 15; };
-template <> struct Emax<kOutE2M1> { static constexpr int value = 2; };
 
 // Magnitude pattern of +Inf in the input type; anything above it is a NaN.
 template <int IN> struct InfBits;
@@ -80,10 +78,11 @@ template <int IN> __device__ __forceinline__ uint32_t widened_exponent(uint32_t 
     }
 }
 
-// E8M0 of one block given the magnitude max over its 32 elements.
-template <int IN, int OUT> __device__ __forceinline__ uint32_t block_e8m0(uint32_t mag)
+// E8M0 of one block given the magnitude max over its 32 elements and the
+// EMAX bias (the format's EMAX, or EMAX - 1 in the alternative mode).
+template <int IN> __device__ __forceinline__ uint32_t block_e8m0(uint32_t mag, int emax_bias)
 {
-    int v = (int)widened_exponent<IN>(mag) - Emax<OUT>::value;
+    int v = (int)widened_exponent<IN>(mag) - emax_bias;
     return (uint32_t)(v < 1 ? 1 : v);
 }
 
@@ -149,18 +148,19 @@ __device__ __forceinline__ uint32_t fp4_bit_offset(uint32_t k)
     return 16u * (k >> 2) + ((0x40C8u >> (4u * (k & 3u))) & 0xFu);
 }
 
-// Rewrite the codes of NaN elements to a zero of the NaN's sign. `w` holds
-// the input dwords of one row of a strip (2*NB of them, element k in the
-// 16-bit half k&1 of w[k/2]); `out` the row's output codes: FP8 byte k of
-// the strip is byte k&3 of out[k/4]; FP4 element k is in out[k/8] at
-// fp4_bit_offset(k mod 8).
+// Rewrite the codes that the conversions cannot give: a NaN element, and
+// every element of a block with E8M0 254, becomes a zero of its own sign.
+// `w` holds the input dwords of one row of a strip (2*NB of them, element k
+// in the 16-bit half k&1 of w[k/2]); `e` the strip's E8M0 bytes; `out` the
+// row's output codes: FP8 byte k of the strip is byte k&3 of out[k/4]; FP4
+// element k is in out[k/8] at fp4_bit_offset(k mod 8).
 template <int IN, int OUT, int NB>
-__device__ __forceinline__ void nan_to_signed_zero(const uint32_t *w, uint32_t *out)
+__device__ __forceinline__ void fix_special_codes(const uint32_t *w, const uint32_t *e, uint32_t *out)
 {
 #pragma unroll
     for (uint32_t k = 0; k < 4 * NB; k++) {
         uint32_t h = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-        if ((h & 0x7FFFu) <= InfBits<IN>::value)
+        if ((h & 0x7FFFu) <= InfBits<IN>::value && e[k >> 2] != 254u)
             continue;
         uint32_t sign = h >> 15;
         if constexpr (OUT == kOutE2M1) {
@@ -258,12 +258,16 @@ template <int XCD> __device__ __forceinline__ uint32_t tile_index()
 //   F          columns (pitch of the input and of FP8 data)
 //   nstrips    F / (4*NB)
 //   ngroups    P / 8
+//   emax_bias  EMAX of the output format, or EMAX - 1 (alternative mode)
+//   dense      0: scale row of group i is (i mod 4) + 32*floor(i/4) of the
+//              P-row image; 1: row i of a dense [P/8, F/4] array
 template <int IN, int OUT, int NB, int GPT, int NT, int XCD = 0>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ in,
                                                        uint8_t *__restrict__ data,
                                                        uint8_t *__restrict__ scale,
                                                        uint64_t F, uint32_t nstrips,
-                                                       uint32_t tiles_per_band, uint32_t ngroups)
+                                                       uint32_t tiles_per_band, uint32_t ngroups,
+                                                       int emax_bias, uint32_t dense)
 {
     static_assert(NB == 1 || NB == 2 || NB == 4, "a strip is 1, 2 or 4 blocks");
     constexpr int LD = NT & 1, ST = (NT >> 1) & 1;
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
         // Block maxima of the magnitude patterns, two 16-bit lanes at a time.
         uint32_t e[NB];
         float s[NB];
-        bool has_nan = false;
+        bool special = false;
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             uint32_t m = 0;
@@ -306,9 +310,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
                 m = pk_max_u16(m, w[j][r][2 * b + 1] & 0x7FFF7FFFu);
             }
             const uint32_t mag = max(m & 0xFFFFu, m >> 16);
-            e[b] = block_e8m0<IN, OUT>(mag);
+            e[b] = block_e8m0<IN>(mag, emax_bias);
             s[b] = e8m0_to_scale(e[b]);
-            has_nan |= mag > InfBits<IN>::value;
+            special |= mag > InfBits<IN>::value || e[b] == 254u;
         }
 
 #pragma unroll
@@ -323,23 +327,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
                     if constexpr (NB > 1)
                         out[h] = fp4_container<IN, 1>(out[h], w[j][r][4 * h + 2], w[j][r][4 * h + 3], s[2 * h + 1]);
                 }
-                if (has_nan)
-                    nan_to_signed_zero<IN, OUT, NB>(w[j][r], out);
+                if (special)
+                    fix_special_codes<IN, OUT, NB>(w[j][r], e, out);
                 store_bytes<2 * NB, ST>(data + (row * F) / 2 + (uint64_t)strip * (2 * NB), out);
             } else {
                 uint32_t out[NB];
 #pragma unroll
                 for (int b = 0; b < NB; b++)
                     out[b] = fp8x4<IN, OUT>(w[j][r][2 * b], w[j][r][2 * b + 1], s[b]);
-                if (has_nan)
-                    nan_to_signed_zero<IN, OUT, NB>(w[j][r], out);
+                if (special)
+                    fix_special_codes<IN, OUT, NB>(w[j][r], e, out);
                 store_bytes<4 * NB, ST>(data + row * F + (uint64_t)strip * (4 * NB), out);
             }
         }
 
         // Scale placement: logical row `group` goes to image row
-        // (group mod 4) + 32 * floor(group / 4).
-        const uint64_t slot = (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
+        // (group mod 4) + 32 * floor(group / 4), or to row `group` of the
+        // dense array.
+        const uint64_t slot = dense ? (uint64_t)group : (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
         uint32_t packed[1] = {0};
 #pragma unroll
         for (int b = 0; b < NB; b++)

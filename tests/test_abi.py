@@ -35,8 +35,9 @@ def _header_enums():
 def test_library_exports_every_declared_function():
     lib = mxq.load()
     names = _declared_functions()
-    assert {"mxq_quantize", "mxq_dequantize", "mxq_data_bytes", "mxq_scale_image_bytes", "mxq_result_bytes",
-            "mxq_status_string", "mxq_abi_version"} <= set(names)
+    assert {"mxq_quantize", "mxq_quantize_ex", "mxq_dequantize", "mxq_dequantize_ex", "mxq_data_bytes",
+            "mxq_scale_image_bytes", "mxq_scale_bytes", "mxq_result_bytes", "mxq_status_string",
+            "mxq_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     # and the shared object's dynamic symbol table has them as functions
@@ -134,6 +135,29 @@ def test_result_bytes():
     assert mxq.result_bytes(16, 8, torch.bfloat16) == 256
     assert mxq.load().mxq_result_bytes(16, 8, 5) == 0
     assert mxq.load().mxq_result_bytes(12, 8, 0) == 0
+
+
+def test_flags():
+    e = _header_enums()
+    text = _header_text()
+    alt = int(re.search(r"MXQ_FLAG_ALT_EMAX (\d+)u", text).group(1))
+    dense = int(re.search(r"MXQ_FLAG_DENSE_SCALE (\d+)u", text).group(1))
+    assert (alt, dense) == (mxq.FLAG_ALT_EMAX, mxq.FLAG_DENSE_SCALE)
+    lib = mxq.load()
+    good = 4096
+    for bad in (4, 8, 1 << 31):
+        assert lib.mxq_quantize_ex(good, 16, 8, 0, 0, bad, good, good, None) == e["MXQ_E_FLAGS"]
+        assert lib.mxq_dequantize_ex(good, good, 16, 8, 0, 0, bad, good, None) == e["MXQ_E_FLAGS"]
+    # the EMAX bias does not enter the dequantize
+    assert lib.mxq_dequantize_ex(good, good, 16, 8, 0, 0, alt, good, None) == e["MXQ_E_FLAGS"]
+    # flags are checked before the shape, shapes before pointers
+    assert lib.mxq_quantize_ex(good, 12, 8, 0, 0, alt | dense, good, good, None) == e["MXQ_E_SHAPE_P8"]
+    assert lib.mxq_quantize_ex(None, 16, 8, 0, 0, alt | dense, good, good, None) == e["MXQ_E_NULL"]
+    assert lib.mxq_scale_bytes(64, 16, 0) == 64 * 4
+    assert lib.mxq_scale_bytes(64, 16, dense) == 8 * 4
+    assert lib.mxq_scale_bytes(64, 16, alt) == 64 * 4
+    assert lib.mxq_scale_bytes(64, 16, 4) == 0
+    assert mxq.scale_image_shape(64, 16, dense_scale=True) == (8, 4)
 
 
 def test_empty_tensors_are_noops():

@@ -26,12 +26,13 @@ def _np_view(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def gpu_dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, fmt: str, res: str) -> np.ndarray:
+def gpu_dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, fmt: str, res: str,
+                   dense: bool = False) -> np.ndarray:
     d = torch.from_numpy(np.ascontiguousarray(data).reshape(mxq.data_shape(P, F, fmt))).cuda()
     im = torch.from_numpy(np.ascontiguousarray(image)).cuda()
     buf = torch.full((P * F + GUARD,), 7.0, dtype=RES[res], device="cuda")
     out = buf[: P * F].view(P, F)
-    mxq.dequantize(d, im, fmt, RES[res], out=out)
+    mxq.dequantize(d, im, fmt, RES[res], out=out, dense_scale=dense)
     torch.cuda.synchronize()
     assert bool((buf[P * F:] == 7.0).all()), "write past the end of the result buffer"
     return _np_view(out)
@@ -71,6 +72,20 @@ def test_random_codes_and_scales(fmt, res, P, F):
     got = gpu_dequantize(data, image, P, F, fmt, res)
     ref = oracle.dequantize(data, image, P, F, fmt, res).reshape(P, F)
     assert_same(got, ref, res, "random")
+
+
+@pytest.mark.parametrize("res", list(RES))
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("P,F", [(8, 4), (40, 12), (264, 1032), (136, 2052)])
+def test_dense_scale_layout(fmt, res, P, F):
+    progress("dequant dense %s->%s %dx%d" % (fmt, res, P, F))
+    rng = np.random.default_rng(P * 7 + F)
+    data = rng.integers(0, 256, size=_data_bytes(P, F, fmt), dtype=np.uint8)
+    dense = rng.integers(0, 256, size=(P // 8, F // 4), dtype=np.uint8)
+    dense[0] = np.resize(np.array([0, 255, 254, 1, 127], np.uint8), dense.shape[1])
+    got = gpu_dequantize(data, dense, P, F, fmt, res, dense=True)
+    ref = oracle.dequantize(data, dense, P, F, fmt, res, layout="dense").reshape(P, F)
+    assert_same(got, ref, res, "dense")
 
 
 @pytest.mark.parametrize("res", list(RES))

@@ -26,26 +26,31 @@ def to_device(x: np.ndarray, in_dtype: str) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(TDT[in_dtype]).to("cuda")
 
 
-def gpu_quantize(xt: torch.Tensor, out: str, stream=None):
+def gpu_quantize(xt: torch.Tensor, out: str, stream=None, alt: bool = False, dense: bool = False):
     """Quantize through the binding into guarded, sentinel-filled buffers.
-    Returns numpy (data, image) after checking the guard band."""
+    Returns numpy (data, scale) after checking the guard bands."""
     P, F = xt.shape
     nbytes = mxq.data_bytes(P, F, out)
     buf = torch.full((nbytes + GUARD,), 0xEE, dtype=torch.uint8, device=xt.device)
     data = buf[:nbytes].view(mxq.data_shape(P, F, out))
-    image = torch.full(mxq.scale_image_shape(P, F), SENTINEL, dtype=torch.uint8, device=xt.device)
-    mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
+    sshape = mxq.scale_image_shape(P, F, dense)
+    sbytes = sshape[0] * sshape[1]
+    sbuf = torch.full((sbytes + GUARD,), SENTINEL, dtype=torch.uint8, device=xt.device)
+    image = sbuf[:sbytes].view(sshape)
+    mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream, alt_emax=alt, dense_scale=dense)
     torch.cuda.synchronize()
-    tail = buf[nbytes:].cpu().numpy()
-    assert np.all(tail == 0xEE), "write past the end of the data buffer"
+    assert np.all(buf[nbytes:].cpu().numpy() == 0xEE), "write past the end of the data buffer"
+    assert np.all(sbuf[sbytes:].cpu().numpy() == SENTINEL), "write past the end of the scale buffer"
     return data.cpu().numpy(), image.cpu().numpy()
 
 
-def check_against_oracle(x: np.ndarray, in_dtype: str, out: str, tag: str):
-    progress("%s %s->%s shape=%s" % (tag, in_dtype, out, x.shape))
-    d_gpu, im_gpu = gpu_quantize(to_device(x, in_dtype), out)
-    fill = np.full((x.shape[0], x.shape[1] // 4), SENTINEL, np.uint8)
-    d_ref, im_ref = oracle.quantize(x, in_dtype, out, image=fill)
+def check_against_oracle(x: np.ndarray, in_dtype: str, out: str, tag: str, alt: bool = False,
+                         dense: bool = False):
+    progress("%s %s->%s shape=%s alt=%d dense=%d" % (tag, in_dtype, out, x.shape, alt, dense))
+    d_gpu, im_gpu = gpu_quantize(to_device(x, in_dtype), out, alt=alt, dense=dense)
+    layout = "dense" if dense else "image"
+    fill = np.full(oracle.scale_shape(x.shape[0], x.shape[1], layout), SENTINEL, np.uint8)
+    d_ref, im_ref = oracle.quantize(x, in_dtype, out, image=fill, alt_emax=alt, layout=layout)
     if not np.array_equal(d_gpu, d_ref):
         bad = np.argwhere(d_gpu != d_ref)
         r, c = bad[0]
@@ -112,10 +117,35 @@ def _pilot_sweep(in_dtype: str) -> np.ndarray:
     return blocks.reshape(nrg, ncb, 8, 4).transpose(0, 2, 1, 3).reshape(nrg * 8, ncb * 4)
 
 
+@pytest.mark.parametrize("alt", (False, True))
 @pytest.mark.parametrize("in_dtype,out", COMBOS)
-def test_exhaustive_pattern_scale_sweep(in_dtype, out):
+def test_exhaustive_pattern_scale_sweep(in_dtype, out, alt):
     x = _pilot_sweep(in_dtype)
-    check_against_oracle(x, in_dtype, out, "sweep")
+    check_against_oracle(x, in_dtype, out, "sweep", alt=alt)
+
+
+MODES = [(True, False), (False, True), (True, True)]
+
+
+@pytest.mark.parametrize("alt,dense", MODES)
+@pytest.mark.parametrize("in_dtype,out", COMBOS)
+@pytest.mark.parametrize("P,F", [(8, 4), (40, 12), (264, 1032), (136, 2052)])
+def test_modes_with_specials(in_dtype, out, P, F, alt, dense):
+    x = workloads.random_bits(P, F, in_dtype, seed=P * 31 + F, specials=True)
+    check_against_oracle(x, in_dtype, out, "mode", alt=alt, dense=dense)
+
+
+@pytest.mark.parametrize("dense", (False, True))
+def test_alt_emax_fp4_nonfinite_blocks(dense):
+    """E8M0 254: every element of a block holding Inf/NaN is a zero of its sign."""
+    P, F = 16, 16
+    x = workloads.random_bits(P, F, "bf16", seed=12)
+    b = x.reshape(P // 8, 8, F // 4, 4)
+    b[0, 0, 0, 0] = 0x7F80
+    b[0, 3, 1, 1] = 0xFF80
+    b[1, 2, 2, 3] = 0xFFC0
+    b[1, 7, 3, 0] = 0x7FC0
+    check_against_oracle(x, "bf16", "e2m1", "alt-nonfinite", alt=True, dense=dense)
 
 
 # ------------------------------------------------------------------ workloads
