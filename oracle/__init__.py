@@ -58,6 +58,9 @@ def _load():
                                               c.c_void_p]
         lib.mxq_oracle_dequantize.restype = c.c_int
         lib.mxq_oracle_f32_to_bf16_array.argtypes = [P_f32, c.c_int64, P_u16]
+        lib.mxq_oracle_scaled_matmul.argtypes = [P_u8, P_u8, P_u8, P_u8, c.c_int64, c.c_int64, c.c_int64,
+                                                 c.c_int, c.c_int, P_f64]
+        lib.mxq_oracle_scaled_matmul.restype = c.c_int
         lib.mxq_oracle_widen_array.argtypes = [P_u16, c.c_int64, c.c_int, P_f32]
         lib.mxq_oracle_narrow_array.argtypes = [P_f32, c.c_int64, c.c_int, P_u8]
         lib.mxq_oracle_prescale_array.argtypes = [P_f32, P_u8, c.c_int64, P_f32]
@@ -137,6 +140,28 @@ def dequantize(data: np.ndarray, image: np.ndarray, P: int, F: int, out_dtype: s
                                    OUT_CODES[out_dtype], RES_CODES[res_dtype], LAYOUTS[layout], out.ctypes.data)
     if rc != 0:
         raise ValueError("oracle dequantize rejected the call (status %d)" % rc)
+    return out
+
+
+def scaled_matmul(lhs: np.ndarray, lhs_scale: np.ndarray, rhs: np.ndarray, rhs_scale: np.ndarray,
+                  fmt: str, layout: str = "image") -> np.ndarray:
+    """out[m][n] = sum_k L[k][m] * R[k][n] in float64, for operands quantized
+    as lhs [P, 4M] and rhs [P, 4N] (x4 containers unpacked along k = 4p + j)."""
+    lib = _load()
+    lhs = np.ascontiguousarray(lhs, dtype=np.uint8)
+    rhs = np.ascontiguousarray(rhs, dtype=np.uint8)
+    ls = np.ascontiguousarray(lhs_scale, dtype=np.uint8)
+    rs = np.ascontiguousarray(rhs_scale, dtype=np.uint8)
+    P = lhs.shape[0]
+    M, N = lhs.shape[1] // 4, rhs.shape[1] // 4
+    if rhs.shape[0] != P:
+        raise ValueError("lhs and rhs must share P")
+    out = np.empty((M, N), dtype=np.float64)
+    rc = lib.mxq_oracle_scaled_matmul(_ptr(lhs, ctypes.c_uint8), _ptr(ls, ctypes.c_uint8), _ptr(rhs, ctypes.c_uint8),
+                                      _ptr(rs, ctypes.c_uint8), P, M, N, OUT_CODES[fmt], LAYOUTS[layout],
+                                      _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle scaled_matmul rejected the call (status %d)" % rc)
     return out
 
 

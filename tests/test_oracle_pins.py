@@ -459,3 +459,75 @@ def test_dequantize_inverts_quantize_on_grid_values(fmt):
     data, image = oracle.quantize(bits, "bf16", fmt)
     back = oracle.dequantize(data, image, P, F, fmt, "f32")
     assert np.array_equal(back, x)
+
+
+# ------------------------------------------------------------- scaled matmul
+
+def _k_major(values_pf: np.ndarray, P: int, C: int) -> np.ndarray:
+    """[P, 4C] element values -> the [K = 4P, C] matrix the reading gives:
+    row k = 4p + j, column c holds element (p, 4c + j)."""
+    return values_pf.reshape(P, C, 4).transpose(0, 2, 1).reshape(4 * P, C)
+
+
+def _operand(rng, P, C, fmt, e_lo, e_hi):
+    codes = rng.integers(0, 256, size=(P, 4 * C), dtype=np.uint8)
+    nan = defcheck.FORMATS[fmt]["maxcode"]          # avoid NaN/Inf codes
+    mag = codes & 0x7F
+    codes = np.where(mag > nan, codes & 0x80 | nan, codes).astype(np.uint8)
+    image = np.zeros((P, C), dtype=np.uint8)
+    image[defcheck.scale_slot(np.arange(P // 8))] = rng.integers(e_lo, e_hi + 1, size=(P // 8, C))
+    return codes, image
+
+
+@pytest.mark.parametrize("fmt", ("e4m3fn", "e5m2"))
+@pytest.mark.parametrize("P,M,N", [(8, 1, 1), (16, 3, 5), (40, 8, 4), (64, 16, 12)])
+def test_scaled_matmul_equals_numpy_matmul_of_dequantized(fmt, P, M, N):
+    """With scales in a narrow band every partial sum is exact in float64,
+    so the triple loop must equal numpy's matmul of the independently
+    dequantized operands bit for bit."""
+    rng = np.random.default_rng(P * 100 + M * 10 + N)
+    lhs, ls = _operand(rng, P, M, fmt, 124, 130)
+    rhs, rs = _operand(rng, P, N, fmt, 124, 130)
+    L = _k_major(defcheck.dequantize(lhs, ls, P, 4 * M, fmt).astype(np.float64), P, M)
+    R = _k_major(defcheck.dequantize(rhs, rs, P, 4 * N, fmt).astype(np.float64), P, N)
+    ref = np.matmul(L.T, R)
+    got = oracle.scaled_matmul(lhs, ls, rhs, rs, fmt)
+    assert np.array_equal(got, ref)
+
+
+def test_scaled_matmul_integer_case():
+    """Codes of small integers at E8M0 127: an exact integer matmul."""
+    rng = np.random.default_rng(5)
+    P, M, N = 16, 6, 7
+    vals = np.array([0.0, 1.0, 2.0, 3.0, 4.0, -1.0, -2.0, -3.0])
+    codes_of = {0.0: 0x00, 1.0: 0x38, 2.0: 0x40, 3.0: 0x44, 4.0: 0x48, -1.0: 0xB8, -2.0: 0xC0, -3.0: 0xC4}
+    li = rng.integers(0, 8, size=(P, 4 * M))
+    ri = rng.integers(0, 8, size=(P, 4 * N))
+    lhs = np.vectorize(lambda i: codes_of[vals[i]])(li).astype(np.uint8)
+    rhs = np.vectorize(lambda i: codes_of[vals[i]])(ri).astype(np.uint8)
+    img_l = np.full((P, M), 127, np.uint8)
+    img_r = np.full((P, N), 127, np.uint8)
+    Lint = _k_major(vals[li], P, M).astype(np.int64)
+    Rint = _k_major(vals[ri], P, N).astype(np.int64)
+    got = oracle.scaled_matmul(lhs, img_l, rhs, img_r, "e4m3fn")
+    assert np.array_equal(got, (Lint.T @ Rint).astype(np.float64))
+
+
+def test_scaled_matmul_hand_worked_and_scale_shift():
+    # K = 32 (one group), M = N = 1: lhs all 1.0 at E8M0 127, rhs all 2.0 at
+    # E8M0 128 (x2): each product is 4, the sum 32 * 4 = 128
+    lhs = np.full((8, 4), 0x38, np.uint8)
+    rhs = np.full((8, 4), 0x40, np.uint8)
+    got = oracle.scaled_matmul(lhs, np.full((8, 1), 127, np.uint8), rhs, np.full((8, 1), 128, np.uint8), "e4m3fn")
+    assert got[0, 0] == 128.0
+    # raising every lhs E8M0 by d multiplies the result by 2^d exactly
+    rng = np.random.default_rng(6)
+    lhs, ls = _operand(rng, 32, 4, "e5m2", 100, 150)
+    rhs, rs = _operand(rng, 32, 3, "e5m2", 100, 150)
+    base = oracle.scaled_matmul(lhs, ls, rhs, rs, "e5m2")
+    placed = defcheck.scale_slot(np.arange(4))
+    ls2 = ls.copy()
+    ls2[placed] += 3
+    assert np.array_equal(oracle.scaled_matmul(lhs, ls2, rhs, rs, "e5m2"), base * 8.0)
+    # the dense layout reads the same scales
+    assert np.array_equal(oracle.scaled_matmul(lhs, ls[placed], rhs, rs[placed], "e5m2", layout="dense"), base)
