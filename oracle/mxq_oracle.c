@@ -510,6 +510,9 @@ int mxq_oracle_dequantize(const uint8_t *data, const uint8_t *scale_image, int64
  * X[k][c] = decode(data[p][4c + j]) * 2^(S[k / 32][c] - 127), where S is the
  * logical scale (row k/32 = row group p/8). The result is
  * out[m][n] = sum_k L[k][m] * R[k][n], formed here in double.
+ * reading: an E8M0 byte of 255 makes its 32 elements NaN here (the OCP MX
+ * meaning of 0xFF); the quantizer never writes it, and the pages' own
+ * dequantize (ldexpf) is kept unchanged by mxq_oracle_dequantize.
  * lhs: P x 4M bytes, rhs: P x 4N bytes; scales as images (or dense arrays).
  * out: M x N doubles, row-major.
  * ---------------------------------------------------------------------- */
@@ -519,6 +522,8 @@ static double operand_value(const uint8_t *data, const uint8_t *scale, int64_t C
     int64_t p = k / 4, j = k % 4;
     double v = mxq_oracle_decode(data[p * 4 * C + 4 * c + j], fmt);
     int e = scale[scale_row(k / 32, scale_layout) * C + c];
+    if (e == 255)
+        return NAN;
     return ldexp(v, e - 127);
 }
 

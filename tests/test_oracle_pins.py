@@ -531,3 +531,16 @@ def test_scaled_matmul_hand_worked_and_scale_shift():
     assert np.array_equal(oracle.scaled_matmul(lhs, ls2, rhs, rs, "e5m2"), base * 8.0)
     # the dense layout reads the same scales
     assert np.array_equal(oracle.scaled_matmul(lhs, ls[placed], rhs, rs[placed], "e5m2", layout="dense"), base)
+
+
+def test_scaled_matmul_e8m0_255_reading():
+    """Reading: an E8M0 of 255 makes its 32 elements NaN in the matmul."""
+    rng = np.random.default_rng(7)
+    lhs, ls = _operand(rng, 16, 3, "e4m3fn", 125, 129)
+    rhs, rs = _operand(rng, 16, 2, "e4m3fn", 125, 129)
+    base = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
+    assert not np.isnan(base).any()
+    ls[defcheck.scale_slot(1), 2] = 255          # row group 1 of lhs column 2
+    got = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
+    assert np.isnan(got[2]).all()
+    assert np.array_equal(np.delete(got, 2, axis=0), np.delete(base, 2, axis=0))
