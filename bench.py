@@ -2,7 +2,7 @@
 """Throughput of the MX quantize on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op quantize|dequantize] [--res bf16|f32]
+                    [--op quantize|dequantize|matmul] [--res bf16|f32]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one full quantize of the workload tensor (one kernel launch: block
@@ -20,6 +20,10 @@ counted.
 ``--op dequantize`` times the inverse instead: the workload is quantized once
 (untimed) and each step decodes it back to ``--res`` (bytes per step = data +
 logical scale + result).
+
+``--op matmul`` times the block-scaled matmul of two quantized e4m3fn
+operands (M = N = 8192, K = 4P = 8192 by default; ``--mm M N K``) in
+TFLOP/s against the matrix cores' dense FP8 peak.
 
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
@@ -41,12 +45,17 @@ if ROOT not in sys.path:
 
 METRIC = "MX quantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
 METRIC_DEQUANT = "MX dequantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
+METRIC_MATMUL = "MX scaled matmul TFLOP/s (fp32 accumulate), 1 MI355X"
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16-131072x8192-colscaled"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "quantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
                  "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
+    "matmul": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
+               "mx_microscaling_quantization_amd/csrc/mxq_matmul_kernels.hpp",
+               "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
     "dequantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
                    "mx_microscaling_quantization_amd/csrc/mxq_dequantize_kernels.hpp",
                    "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
@@ -151,6 +160,93 @@ def cpu_baseline_dequant(data, image, fmt: str, res: str, budget_s: float = 12.0
                       % (done_rows, P, done_rows, F, spent)}
 
 
+def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block: int = 16):
+    """The CPU oracle's scaled matmul (single thread) on block x block output
+    tiles along the diagonal until about budget_s seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    oracle.build(force=False)
+    P = dl.shape[0]
+    M, N = dl.shape[1] // 4, dr.shape[1] // 4
+    done, spent = 0, 0.0
+    while spent < budget_s and (done + 1) * block <= min(M, N):
+        c0 = done * block
+        hl = dl[:, 4 * c0:4 * (c0 + block)].contiguous().cpu().numpy()
+        hr = dr[:, 4 * c0:4 * (c0 + block)].contiguous().cpu().numpy()
+        hsl = sl[:, c0:c0 + block].contiguous().cpu().numpy()
+        hsr = sr[:, c0:c0 + block].contiguous().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.scaled_matmul(hl, hsl, hr, hsr, fmt)
+        spent += time.perf_counter() - t0
+        done += 1
+    flops = 2.0 * done * block * block * 4 * P
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "%d diagonal %dx%d output tiles at K=%d (%.3g s of single-thread oracle time)"
+                      % (done, block, block, 4 * P, spent)}
+
+
+def bench_matmul(args) -> int:
+    import torch
+
+    import mx_microscaling_quantization_amd as mxq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, N, K = args.mm
+    P = K // 4
+    fmt = "e4m3fn"
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    xl = torch.randn((P, 4 * M), generator=g, device=dev).to(torch.bfloat16)
+    xr = torch.randn((P, 4 * N), generator=g, device=dev).to(torch.bfloat16)
+    dl, sl = mxq.quantize(xl, fmt)
+    dr, sr = mxq.quantize(xr, fmt)
+    del xl, xr
+    res_t = torch.bfloat16 if args.res == "bf16" else torch.float32
+    out = torch.empty((M, N), dtype=res_t, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mxq.scaled_matmul(dl, sl, dr, sr, fmt, res_t, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_begin.record(stream)
+    for k in range(args.steps):
+        starts[k].record(stream)
+        step()
+        ends[k].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    avg_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    flops = 2.0 * M * N * K
+    value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC_MATMUL, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic",
+        "config": {"workload": "%s-%dx%dx%d-scaled-matmul" % (fmt, M, N, K), "M": M, "N": N, "K": K,
+                   "out": args.res, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_avg_us": round(avg_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_matmul(dl, sl, dr, sr, fmt)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def copy_calibration(steps: int, warmup: int) -> None:
     import torch
 
@@ -178,7 +274,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--out", default=None, help="output format (default: the workload's first)")
-    ap.add_argument("--op", choices=("quantize", "dequantize"), default="quantize")
+    ap.add_argument("--op", choices=("quantize", "dequantize", "matmul"), default="quantize")
+    ap.add_argument("--mm", type=int, nargs=3, default=(8192, 8192, 8192), metavar=("M", "N", "K"),
+                    help="matmul sizes (M, N multiples of 4, K a multiple of 32)")
     ap.add_argument("--res", choices=("bf16", "f32"), default="bf16", help="dequantize result type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -202,6 +300,8 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.steps, args.warmup)
         return 0
+    if args.op == "matmul":
+        return bench_matmul(args)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -171,6 +171,44 @@ int mxq_dequantize_ex(const void *data, const void *scale_in, int64_t P, int64_t
  * invalid arguments. */
 size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype);
 
+/*
+ * mxq_scaled_matmul -- block-scaled matmul of two MX-quantized operands.
+ *
+ * The consumer of the quantize: "MX-FP8 Microscaling Legalization",
+ * LegalizeScaledMatmul (four operands lhs, rhs, lhs_scale, rhs_scale; both
+ * operands in one FP8 format; an F32 or BF16 result) and the crosswalk
+ * (a 32-element group is 8 partitions x 4 elements; each x4 container
+ * unpacks into the contraction dimension); element values as for
+ * mxq_dequantize.
+ *
+ * Reading of the operand layout: an operand quantized by mxq_quantize as a
+ * P x F tensor (F = 4C) is the K x C matrix X[k][c], k = 4p + j (p the row,
+ * j the element's place in its x4 container, K = 4P), c the container index
+ * (f / 4), X[k][c] = decode(q) * 2^(E8M0 - 127) with the E8M0 of row group
+ * k / 32. The result is
+ *     out[m][n] = sum over k < 4P of L[k][m] * R[k][n]
+ * accumulated in fp32 (MFMA; the summation order is the hardware's).
+ * An E8M0 byte of 255 makes its 32 elements NaN (this consumer follows the
+ * OCP reading of 0xFF; the quantizer never writes it).
+ *
+ *   lhs, lhs_scale  P x 4M FP8 data and its scale image (P x M), as
+ *                   mxq_quantize(P, F = 4M) writes them.
+ *   rhs, rhs_scale  P x 4N FP8 data and its scale image (P x N).
+ *   P               multiple of 8 (K = 4P a multiple of 32); P == 0 gives a
+ *                   zero result (the operand pointers may then be NULL).
+ *   M, N            multiples of 4; M == 0 or N == 0 is an empty call.
+ *   fmt             MXQ_OUT_E4M3FN or MXQ_OUT_E5M2 (both operands).
+ *   res_dtype       MXQ_RES_F32 or MXQ_RES_BF16 (the fp32 sum rounded to
+ *                   nearest-even).
+ *   flags           MXQ_FLAG_DENSE_SCALE: both scales are dense [P/8, C].
+ *   out             M x N results, row-major, 16-byte aligned.
+ *   stream          hipStream_t of the current device (NULL = default).
+ * All pointers are device pointers, 16-byte aligned. Returns MXQ_OK once
+ * enqueued, else an MXQ_E_* code with nothing enqueued.
+ */
+int mxq_scaled_matmul(const void *lhs, const void *lhs_scale, const void *rhs, const void *rhs_scale, int64_t P,
+                      int64_t M, int64_t N, int fmt, int res_dtype, unsigned flags, void *out, void *stream);
+
 /* Human-readable message for a status code (static storage, never NULL). */
 const char *mxq_status_string(int status);
 

@@ -16,7 +16,7 @@ import threading
 import torch  # loaded first so that the library binds to torch's HIP runtime
 
 __all__ = [
-    "IN_DTYPES", "OUT_DTYPES", "RES_DTYPES", "MXQError", "quantize", "dequantize", "data_bytes",
+    "IN_DTYPES", "OUT_DTYPES", "RES_DTYPES", "MXQError", "quantize", "dequantize", "scaled_matmul", "data_bytes",
     "scale_image_bytes", "result_bytes", "data_shape", "scale_image_shape", "logical_scale_view",
     "status_string", "library_path", "load",
 ]
@@ -67,6 +67,9 @@ def load():
         lib.mxq_dequantize_ex.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int,
                                           c.c_uint, c.c_void_p, c.c_void_p]
         lib.mxq_dequantize_ex.restype = c.c_int
+        lib.mxq_scaled_matmul.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_int64,
+                                          c.c_int64, c.c_int, c.c_int, c.c_uint, c.c_void_p, c.c_void_p]
+        lib.mxq_scaled_matmul.restype = c.c_int
         lib.mxq_scale_bytes.argtypes = [c.c_int64, c.c_int64, c.c_uint]
         lib.mxq_scale_bytes.restype = c.c_size_t
         lib.mxq_data_bytes.argtypes = [c.c_int64, c.c_int64, c.c_int]
@@ -213,4 +216,43 @@ def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "
     with torch.cuda.device(data.device):
         _check(lib.mxq_dequantize_ex(data.data_ptr(), scale_image.data_ptr(), P, F, code, RES_DTYPES[res_dtype],
                                      FLAG_DENSE_SCALE if dense_scale else 0, out.data_ptr(), stream.cuda_stream))
+    return out
+
+
+def scaled_matmul(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor, rhs_scale: torch.Tensor,
+                  fmt: str = "e4m3fn", res_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None,
+                  stream: torch.cuda.Stream | None = None, dense_scale: bool = False) -> torch.Tensor:
+    """Block-scaled matmul of two quantized operands.
+
+    ``lhs`` [P, 4M] and ``rhs`` [P, 4N] are FP8 data outputs of
+    :func:`quantize` (format ``fmt``) with their scale images ``lhs_scale``
+    [P, M] and ``rhs_scale`` [P, N] (or dense [P/8, M], [P/8, N] with
+    ``dense_scale``). Each operand is read as the [K = 4P, C] matrix whose
+    row k = 4p + j holds element (p, 4c + j). Returns
+    out[m][n] = sum_k L[k][m] * R[k][n] as [M, N] float32 or bfloat16.
+    """
+    lib = load()
+    code = _out_code(fmt)
+    if res_dtype not in RES_DTYPES:
+        raise MXQError(10, "result type must be float32 or bfloat16, got %s" % res_dtype)
+    for t in (lhs, lhs_scale, rhs, rhs_scale):
+        if t.dim() != 2 or t.dtype != torch.uint8 or not t.is_contiguous() or t.device != lhs.device or not t.is_cuda:
+            raise ValueError("operands must be contiguous 2-D uint8 device tensors on one device")
+    P = lhs.shape[0]
+    M, N = lhs.shape[1] // 4, rhs.shape[1] // 4
+    if rhs.shape[0] != P or lhs.shape[1] % 4 or rhs.shape[1] % 4:
+        raise ValueError("lhs [P, 4M] and rhs [P, 4N] must share P")
+    if tuple(lhs_scale.shape) != scale_image_shape(P, 4 * M, dense_scale) or \
+            tuple(rhs_scale.shape) != scale_image_shape(P, 4 * N, dense_scale):
+        raise ValueError("scale shapes do not match the operands")
+    if out is None:
+        out = torch.empty((M, N), dtype=res_dtype, device=lhs.device)
+    elif out.dtype != res_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous() or out.device != lhs.device:
+        raise ValueError("out must be a contiguous [%d, %d] %s tensor on %s" % (M, N, res_dtype, lhs.device))
+    if stream is None:
+        stream = torch.cuda.current_stream(lhs.device)
+    with torch.cuda.device(lhs.device):
+        _check(lib.mxq_scaled_matmul(lhs.data_ptr(), lhs_scale.data_ptr(), rhs.data_ptr(), rhs_scale.data_ptr(), P, M, N,
+                                     code, RES_DTYPES[res_dtype], FLAG_DENSE_SCALE if dense_scale else 0,
+                                     out.data_ptr(), stream.cuda_stream))
     return out

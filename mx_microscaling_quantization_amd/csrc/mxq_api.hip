@@ -8,6 +8,7 @@
 
 #include "mxq.h"
 #include "mxq_dequantize_kernels.hpp"
+#include "mxq_matmul_kernels.hpp"
 #include "mxq_quantize_kernels.hpp"
 
 namespace {
@@ -71,6 +72,15 @@ int emax_of(int out_dtype)
     case MXQ_OUT_E5M2: return 15;
     default: return 2;
     }
+}
+
+typedef void (*mm_kernel_fn)(const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, uint32_t, uint32_t,
+                             uint32_t, uint32_t, uint32_t, void *);
+
+template <int FMT> mm_kernel_fn mm_pick_res(int res)
+{
+    return res == MXQ_RES_F32 ? (mm_kernel_fn)mxq::scaled_matmul_kernel<FMT, 0>
+                              : (mm_kernel_fn)mxq::scaled_matmul_kernel<FMT, 1>;
 }
 
 int check_shape(int64_t P, int64_t F)
@@ -193,6 +203,48 @@ int mxq_dequantize_ex(const void *data, const void *scale_in, int64_t P, int64_t
     void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6};
     hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(groups * tiles_per_group)), dim3(kThreads),
                                      args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
+}
+
+int mxq_scaled_matmul(const void *lhs, const void *lhs_scale, const void *rhs, const void *rhs_scale, int64_t P,
+                      int64_t M, int64_t N, int fmt, int res_dtype, unsigned flags, void *out, void *stream)
+{
+    if (fmt != MXQ_OUT_E4M3FN && fmt != MXQ_OUT_E5M2)
+        return MXQ_E_OUT_DTYPE;
+    if (res_dtype != MXQ_RES_F32 && res_dtype != MXQ_RES_BF16)
+        return MXQ_E_RES_DTYPE;
+    if (flags & ~(unsigned)MXQ_FLAG_DENSE_SCALE)
+        return MXQ_E_FLAGS;
+    if (P < 0 || P % 8 != 0)
+        return MXQ_E_SHAPE_P8;
+    if (M < 0 || N < 0 || M % 4 != 0 || N % 4 != 0)
+        return MXQ_E_SHAPE_F4;
+    const int64_t kMax = ((int64_t)1 << 31) - 1;
+    if (P > kMax || 4 * M > kMax || 4 * N > kMax)
+        return MXQ_E_OVERFLOW;
+    if (M == 0 || N == 0)
+        return MXQ_OK;
+    if (!out || (P > 0 && (!lhs || !lhs_scale || !rhs || !rhs_scale)))
+        return MXQ_E_NULL; // with P == 0 the operands are empty and never read
+    if (((uintptr_t)lhs | (uintptr_t)lhs_scale | (uintptr_t)rhs | (uintptr_t)rhs_scale | (uintptr_t)out) & 15u)
+        return MXQ_E_ALIGN;
+    const int64_t tiles_m = (M + mxq::kMmTile - 1) / mxq::kMmTile;
+    const int64_t tiles_n = (N + mxq::kMmTile - 1) / mxq::kMmTile;
+    if (tiles_m > kMax / tiles_n)
+        return MXQ_E_OVERFLOW;
+
+    mm_kernel_fn k = fmt == MXQ_OUT_E4M3FN ? mm_pick_res<mxq::kOutE4M3FN>(res_dtype)
+                                           : mm_pick_res<mxq::kOutE5M2>(res_dtype);
+    const uint8_t *a0 = (const uint8_t *)lhs;
+    const uint8_t *a1 = (const uint8_t *)lhs_scale;
+    const uint8_t *a2 = (const uint8_t *)rhs;
+    const uint8_t *a3 = (const uint8_t *)rhs_scale;
+    uint32_t a4 = (uint32_t)P, a5 = (uint32_t)M, a6 = (uint32_t)N, a7 = (uint32_t)tiles_n;
+    uint32_t a8 = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
+    void *a9 = out;
+    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7, &a8, &a9};
+    hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(tiles_m * tiles_n)), dim3(mxq::kMmThreads), args,
+                                     0, (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
 }
 

@@ -35,7 +35,8 @@ def _header_enums():
 def test_library_exports_every_declared_function():
     lib = mxq.load()
     names = _declared_functions()
-    assert {"mxq_quantize", "mxq_quantize_ex", "mxq_dequantize", "mxq_dequantize_ex", "mxq_data_bytes",
+    assert {"mxq_quantize", "mxq_quantize_ex", "mxq_dequantize", "mxq_dequantize_ex", "mxq_scaled_matmul",
+            "mxq_data_bytes",
             "mxq_scale_image_bytes", "mxq_scale_bytes", "mxq_result_bytes", "mxq_status_string",
             "mxq_abi_version"} <= set(names)
     for name in names:
@@ -158,6 +159,30 @@ def test_flags():
     assert lib.mxq_scale_bytes(64, 16, alt) == 64 * 4
     assert lib.mxq_scale_bytes(64, 16, 4) == 0
     assert mxq.scale_image_shape(64, 16, dense_scale=True) == (8, 4)
+
+
+def test_scaled_matmul_validation_errors_before_launch():
+    e = _header_enums()
+    lib = mxq.load()
+    g = 4096
+
+    def mm(P, M, N, fmt=0, res=0, flags=0, ptrs=(g, g, g, g, g)):
+        a, b, c, d, o = ptrs
+        return lib.mxq_scaled_matmul(a, b, c, d, P, M, N, fmt, res, flags, o, None)
+
+    assert mm(32, 4, 4, fmt=2) == e["MXQ_E_OUT_DTYPE"]          # FP4 is not a ScaledMatmul element type
+    assert mm(32, 4, 4, fmt=3) == e["MXQ_E_OUT_DTYPE"]
+    assert mm(32, 4, 4, res=2) == e["MXQ_E_RES_DTYPE"]
+    assert mm(32, 4, 4, flags=1) == e["MXQ_E_FLAGS"]
+    assert mm(12, 4, 4) == e["MXQ_E_SHAPE_P8"]
+    assert mm(32, 6, 4) == e["MXQ_E_SHAPE_F4"]
+    assert mm(32, 4, 2) == e["MXQ_E_SHAPE_F4"]
+    assert mm(1 << 32, 4, 4) == e["MXQ_E_OVERFLOW"]
+    assert mm(32, 0, 4, ptrs=(None,) * 5) == 0
+    assert mm(32, 4, 0, ptrs=(None,) * 5) == 0
+    assert mm(32, 4, 4, ptrs=(g, g, None, g, g)) == e["MXQ_E_NULL"]
+    assert mm(0, 4, 4, ptrs=(g, g, g, g, None)) == e["MXQ_E_NULL"]
+    assert mm(32, 4, 4, ptrs=(g, g, g, g + 4, g)) == e["MXQ_E_ALIGN"]
 
 
 def test_empty_tensors_are_noops():
