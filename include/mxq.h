@@ -197,6 +197,8 @@ size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype);
  *   P               multiple of 8 (K = 4P a multiple of 32); P == 0 gives a
  *                   zero result (the operand pointers may then be NULL).
  *   M, N            multiples of 4; M == 0 or N == 0 is an empty call.
+ *                   M, N <= MXQ_MATMUL_MAX_COLS, else MXQ_E_OVERFLOW (the
+ *                   kernel addresses 32 operand rows with 32-bit offsets).
  *   fmt             MXQ_OUT_E4M3FN or MXQ_OUT_E5M2 (both operands).
  *   res_dtype       MXQ_RES_F32 or MXQ_RES_BF16 (the fp32 sum rounded to
  *                   nearest-even).
@@ -206,6 +208,8 @@ size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype);
  * All pointers are device pointers, 16-byte aligned. Returns MXQ_OK once
  * enqueued, else an MXQ_E_* code with nothing enqueued.
  */
+#define MXQ_MATMUL_MAX_COLS 33554176 /* 2^25 - 256 containers per operand row */
+
 int mxq_scaled_matmul(const void *lhs, const void *lhs_scale, const void *rhs, const void *rhs_scale, int64_t P,
                       int64_t M, int64_t N, int fmt, int res_dtype, unsigned flags, void *out, void *stream);
 

@@ -220,7 +220,7 @@ int mxq_scaled_matmul(const void *lhs, const void *lhs_scale, const void *rhs, c
     if (M < 0 || N < 0 || M % 4 != 0 || N % 4 != 0)
         return MXQ_E_SHAPE_F4;
     const int64_t kMax = ((int64_t)1 << 31) - 1;
-    if (P > kMax || 4 * M > kMax || 4 * N > kMax)
+    if (P > kMax || M > MXQ_MATMUL_MAX_COLS || N > MXQ_MATMUL_MAX_COLS)
         return MXQ_E_OVERFLOW;
     if (M == 0 || N == 0)
         return MXQ_OK;

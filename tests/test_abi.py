@@ -29,6 +29,8 @@ def _header_enums():
     vals = {}
     for name, val in re.findall(r"\b(MXQ_[A-Z0-9_]+)\s*=\s*(\d+)", _header_text()):
         vals[name] = int(val)
+    for name, val in re.findall(r"#define\s+(MXQ_[A-Z0-9_]+)\s+(\d+)u?\b", _header_text()):
+        vals[name] = int(val)
     return vals
 
 
@@ -178,6 +180,10 @@ def test_scaled_matmul_validation_errors_before_launch():
     assert mm(32, 6, 4) == e["MXQ_E_SHAPE_F4"]
     assert mm(32, 4, 2) == e["MXQ_E_SHAPE_F4"]
     assert mm(1 << 32, 4, 4) == e["MXQ_E_OVERFLOW"]
+    cap = e["MXQ_MATMUL_MAX_COLS"]
+    assert mm(32, cap + 4, 4) == e["MXQ_E_OVERFLOW"]             # 32-row offsets must fit 32 bits
+    assert mm(32, 4, cap + 4) == e["MXQ_E_OVERFLOW"]
+    assert 32 * 4 * cap + 1024 < 1 << 32
     assert mm(32, 0, 4, ptrs=(None,) * 5) == 0
     assert mm(32, 4, 0, ptrs=(None,) * 5) == 0
     assert mm(32, 4, 4, ptrs=(g, g, None, g, g)) == e["MXQ_E_NULL"]
