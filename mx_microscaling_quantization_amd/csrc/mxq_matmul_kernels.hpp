@@ -54,6 +54,8 @@ constexpr int kMmStepRows = 32;     // operand rows per K step (K = 128)
 constexpr int kMmThreads = 256;
 constexpr int kMmXcds = 8;
 constexpr int kMmGroupRows = 4;     // tile rows walked together (L2 reuse)
+constexpr int kMmStashA = 2;        // row tile that writes the next A tile (next: its loads)
+constexpr int kMmStashB = 4;        // row tile that writes the next B tile (next: its loads)
 
 // MFMA operand-format code of an element format (cbsz / blgp field).
 template <int FMT> struct MfmaFmt;
@@ -216,15 +218,18 @@ __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
         for (int b = 0; b < kMmSub; b++)
             acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Software pipeline, per K step s (stage s & 1 holds step s):
-    //   row tiles 0..7: 8 MFMAs each, reading the next row tile's A operand;
-    //   row tile 3 / 4: write step s + 1's A / B tile (in registers since
-    //     the middle of step s - 1) into the other stage, then issue the
-    //     global loads of step s + 2 into the freed registers;
+    // Software pipeline, per K step s (stage s & 1 holds step s). Each row
+    // tile issues 8 MFMAs and reads the next row tile's A operand; besides,
+    //   row tile 2 / 4: write step s + 1's A / B tile (in registers since
+    //     step s - 1) into the other stage, one 16-byte LDS write per MFMA;
+    //   row tile 3 / 5: issue the global loads of step s + 2 into the freed
+    //     registers, one load per MFMA;
     //   row tile 7: one barrier (every wave has written step s + 1 and read
     //     its last operand of step s), then step s + 1's B operands and
     //     first A operand are read between the last 8 MFMAs.
-    // sched_barrier keeps the compiler from hoisting those phases.
+    // With one wave per SIMD and in-order issue, a burst of loads or LDS
+    // writes would stall the matrix core, so sched_group_barrier spreads
+    // them between the MFMAs; sched_barrier fences the row tiles.
     MmFetch fa, fb;
     mm_fetch(fa, src_a, P, 0, wave, dense, lane);
     mm_fetch(fb, src_b, P, 0, wave, dense, lane);
@@ -266,29 +271,41 @@ __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
                 an = mm_operand(nxt, a_lo, a_hi, 0);
                 ans = nxt[2 * kMmTileBytes + a_sc];
             }
+            // The loop body is one basic block, so nothing here is
+            // conditional: on the last step the stash writes the other stage
+            // (free since the previous barrier, never read again) and the
+            // loads past the end read nothing.
+            if (a == kMmStashA)
+                mm_stash(fa, nxt, nxt + 2 * kMmTileBytes, st0, st1, tid);
+            if (a == kMmStashA + 1)
+                mm_fetch(fa, src_a, P, s + 2, wave, dense, lane);
+            if (a == kMmStashB)
+                mm_stash(fb, nxt + kMmTileBytes, nxt + 2 * kMmTileBytes + kMmScaleBytes, st0, st1, tid);
+            if (a == kMmStashB + 1)
+                mm_fetch(fb, src_b, P, s + 2, wave, dense, lane);
 #pragma unroll
             for (int b = 0; b < kMmSub; b++) {
                 acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[b], acc[a][b], F, F, 0, asc,
                                                                              0, bsc[b]);
                 if (a == kMmSub - 1) {
-                    __builtin_amdgcn_sched_barrier(0);
                     bop[b] = mm_operand(nxt + kMmTileBytes, b_lo, b_hi, b);
                     bsc[b] = nxt[2 * kMmTileBytes + kMmScaleBytes + b_sc + 16u * b];
                 }
             }
-            // The loop body is one basic block, so nothing here is
-            // conditional: on the last step the stash writes the other stage
-            // (free since the previous barrier, never read again) and the
-            // loads past the end read nothing.
-            if (a == 3) {
-                __builtin_amdgcn_sched_barrier(0);
-                mm_stash(fa, nxt, nxt + 2 * kMmTileBytes, st0, st1, tid);
-                mm_fetch(fa, src_a, P, s + 2, wave, dense, lane);
-            }
-            if (a == 4) {
-                __builtin_amdgcn_sched_barrier(0);
-                mm_stash(fb, nxt + kMmTileBytes, nxt + 2 * kMmTileBytes + kMmScaleBytes, st0, st1, tid);
-                mm_fetch(fb, src_b, P, s + 2, wave, dense, lane);
+            // instruction order inside the row tile (masks: 0x008 MFMA,
+            // 0x100 LDS read, 0x200 LDS write, 0x020 global load, 0x002 VALU)
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);          // next A operand first
+#pragma unroll
+            for (int b = 0; b < kMmSub; b++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (a == kMmSub - 1) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next step's B operand b
+                } else if (a == kMmStashA || a == kMmStashB) {
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // gather one row quad
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // and write it
+                } else if (a == kMmStashA + 1 || a == kMmStashB + 1) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
             }
             aop = an;
             asc = ans;
