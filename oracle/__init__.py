@@ -61,6 +61,9 @@ def _load():
         lib.mxq_oracle_scaled_matmul.argtypes = [P_u8, P_u8, P_u8, P_u8, c.c_int64, c.c_int64, c.c_int64,
                                                  c.c_int, c.c_int, P_f64]
         lib.mxq_oracle_scaled_matmul.restype = c.c_int
+        lib.mxq_oracle_scaled_matmul_quantize.argtypes = [P_u8, P_u8, P_u8, P_u8, c.c_int64, c.c_int64, c.c_int64,
+                                                          c.c_int, c.c_int, c.c_int, c.c_int, P_u8, P_u8]
+        lib.mxq_oracle_scaled_matmul_quantize.restype = c.c_int
         lib.mxq_oracle_widen_array.argtypes = [P_u16, c.c_int64, c.c_int, P_f32]
         lib.mxq_oracle_narrow_array.argtypes = [P_f32, c.c_int64, c.c_int, P_u8]
         lib.mxq_oracle_prescale_array.argtypes = [P_f32, P_u8, c.c_int64, P_f32]
@@ -163,6 +166,33 @@ def scaled_matmul(lhs: np.ndarray, lhs_scale: np.ndarray, rhs: np.ndarray, rhs_s
     if rc != 0:
         raise ValueError("oracle scaled_matmul rejected the call (status %d)" % rc)
     return out
+
+
+def scaled_matmul_quantize(lhs: np.ndarray, lhs_scale: np.ndarray, rhs: np.ndarray, rhs_scale: np.ndarray,
+                           fmt: str, out_dtype: str, alt_emax: bool = False, layout: str = "image"):
+    """quantize(bf16(scaled_matmul(...))): the M x N matmul result rounded to
+    fp32 then bf16 and quantized (8 x 4 blocks over rows m, columns n).
+    Returns ``(data, scale)`` shaped as :func:`quantize` would for P = M,
+    F = N; operand and result scales share ``layout``."""
+    lib = _load()
+    lhs = np.ascontiguousarray(lhs, dtype=np.uint8)
+    rhs = np.ascontiguousarray(rhs, dtype=np.uint8)
+    ls = np.ascontiguousarray(lhs_scale, dtype=np.uint8)
+    rs = np.ascontiguousarray(rhs_scale, dtype=np.uint8)
+    P = lhs.shape[0]
+    M, N = lhs.shape[1] // 4, rhs.shape[1] // 4
+    if rhs.shape[0] != P:
+        raise ValueError("lhs and rhs must share P")
+    data = np.zeros(data_shape(M, N, out_dtype), dtype=np.uint8)
+    scale = np.zeros(scale_shape(M, N, layout), dtype=np.uint8)
+    rc = lib.mxq_oracle_scaled_matmul_quantize(_ptr(lhs, ctypes.c_uint8), _ptr(ls, ctypes.c_uint8),
+                                               _ptr(rhs, ctypes.c_uint8), _ptr(rs, ctypes.c_uint8), P, M, N,
+                                               OUT_CODES[fmt], OUT_CODES[out_dtype], int(bool(alt_emax)),
+                                               LAYOUTS[layout], _ptr(data, ctypes.c_uint8),
+                                               _ptr(scale, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle scaled_matmul_quantize rejected the call (status %d)" % rc)
+    return data, scale
 
 
 def f32_to_bf16(f: np.ndarray) -> np.ndarray:

@@ -552,6 +552,50 @@ int mxq_oracle_scaled_matmul(const uint8_t *lhs, const uint8_t *lhs_scale, const
 }
 
 /* ------------------------------------------------------------------------
+ * Quantize-on-produce: the matmul's result quantized for the next consumer.
+ * [LEG] "The pipeline coupling": the quantize produces the operands of the
+ * scaled matmul and the two compose by dataflow, so in an MX network the
+ * next layer's quantize consumes the matmul's result.
+ * reading: the fused result is quantize(bf16(out)) -- the exact sum rounded
+ * to fp32 (the accumulator type), then to nearest-even bf16 (the matmul's
+ * BF16 result type, which the quantize takes), then the quantize of that
+ * M x N bf16 tensor (blocks of 8 rows m x 4 columns n). Fusing changes no
+ * byte of that composition.
+ * data_out / scale_out as mxq_oracle_quantize(P = M, F = N); the operand
+ * scales and the result scale share scale_layout.
+ * ---------------------------------------------------------------------- */
+int mxq_oracle_scaled_matmul_quantize(const uint8_t *lhs, const uint8_t *lhs_scale, const uint8_t *rhs,
+                                      const uint8_t *rhs_scale, int64_t P, int64_t M, int64_t N, int fmt,
+                                      int out_dtype, int alt_emax, int scale_layout, uint8_t *data_out,
+                                      uint8_t *scale_out)
+{
+    if (mxq_oracle_emax(out_dtype) < 0)
+        return ORC_BAD_OUT_DTYPE;
+    if (M < 0 || M % 8 != 0)
+        return ORC_BAD_P;
+    if (N < 0 || N % 4 != 0)
+        return ORC_BAD_F;
+    if (M == 0 || N == 0)
+        return mxq_oracle_scaled_matmul(lhs, lhs_scale, rhs, rhs_scale, P, M, N, fmt, scale_layout, NULL);
+    double *sum = (double *)malloc((size_t)(M * N) * sizeof(double));
+    uint16_t *res = (uint16_t *)malloc((size_t)(M * N) * sizeof(uint16_t));
+    if (!sum || !res) {
+        free(sum);
+        free(res);
+        return ORC_NO_MEMORY;
+    }
+    int rc = mxq_oracle_scaled_matmul(lhs, lhs_scale, rhs, rhs_scale, P, M, N, fmt, scale_layout, sum);
+    if (rc == ORC_OK) {
+        for (int64_t k = 0; k < M * N; k++)
+            res[k] = mxq_oracle_f32_to_bf16((float)sum[k]); /* double -> float rounds to nearest-even */
+        rc = mxq_oracle_quantize(res, M, N, ORC_IN_BF16, out_dtype, alt_emax, scale_layout, data_out, scale_out);
+    }
+    free(sum);
+    free(res);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
  * Array helpers so that exhaustive pins do not pay one foreign call per
  * value. Each applies one of the steps above element by element.
  * ---------------------------------------------------------------------- */

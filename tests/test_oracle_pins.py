@@ -544,3 +544,70 @@ def test_scaled_matmul_e8m0_255_reading():
     got = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
     assert np.isnan(got[2]).all()
     assert np.array_equal(np.delete(got, 2, axis=0), np.delete(base, 2, axis=0))
+
+
+# ------------------------------------------------------ quantize-on-produce
+
+@pytest.mark.parametrize("fmt,out", [("e4m3fn", "e4m3fn"), ("e5m2", "e5m2"), ("e4m3fn", "e2m1"),
+                                     ("e5m2", "e4m3fn")])
+@pytest.mark.parametrize("alt,layout", [(False, "image"), (True, "dense")])
+def test_scaled_matmul_quantize_equals_definition_composition(fmt, out, alt, layout):
+    """The fused oracle equals the definition checker's quantize of the
+    product rounded to fp32 and then to bf16. The exact product comes from
+    numpy's float64 matmul of the independently dequantized operands (scales
+    in a narrow band keep every partial sum exact) and the bf16 rounding from
+    torch's nearest-even cast, so no step is the oracle's own."""
+    import torch
+
+    P, M, N = 32, 16, 12
+    rng = np.random.default_rng(sum(map(ord, fmt + out)) + 2 * alt)
+    lhs, ls = _operand(rng, P, M, fmt, 124, 130)
+    rhs, rs = _operand(rng, P, N, fmt, 124, 130)
+    L = _k_major(defcheck.dequantize(lhs, ls, P, 4 * M, fmt).astype(np.float64), P, M)
+    R = _k_major(defcheck.dequantize(rhs, rs, P, 4 * N, fmt).astype(np.float64), P, N)
+    exact = np.matmul(L.T, R)
+    b16 = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    want_data, want_scale = defcheck.quantize(b16, "bf16", out, alt=alt, layout=layout)
+    if layout == "dense":
+        placed = defcheck.scale_slot(np.arange(P // 8))
+        ls, rs = ls[placed], rs[placed]
+    got_data, got_scale = oracle.scaled_matmul_quantize(lhs, ls, rhs, rs, fmt, out, alt_emax=alt, layout=layout)
+    assert np.array_equal(got_data, want_data)
+    assert np.array_equal(got_scale, want_scale)
+
+
+def test_scaled_matmul_quantize_rounds_through_bf16():
+    """Hand-worked, e4m3fn in and out, every E8M0 127 (scale 1). Column 0 of
+    rhs holds 30 codes of 1.0, one 4.0 (0x48) and one 2^-4 (0x18); lhs is all
+    1.0, so out[m][0] = 34.0625 for every m, and columns 1..3 are 0.
+      bf16 keeps 8 significant bits: between 32 and 64 its step is 0.25, and
+      34.0625 rounds to 34.0.
+      Block max 34 has exponent 5, so E8M0 = 127 + 5 - 8 = 124 and the
+      prescale multiplies by 2^(127 - 124) = 8: 34 -> 272, the midpoint of
+      the e4m3fn neighbours 256 (0x78) and 288 (0x79); nearest-even gives
+      0x78. Quantizing the fp32 value instead (272.5) would give 0x79."""
+    lhs = np.full((8, 4 * 8), 0x38, np.uint8)                   # M = 8 columns of 1.0
+    rhs = np.zeros((8, 4 * 4), np.uint8)                        # N = 4
+    rhs[:, 0:4] = 0x38
+    rhs[0, 0] = 0x48                                            # 4.0
+    rhs[0, 1] = 0x18                                            # 2^-4
+    ls = np.full((8, 8), 127, np.uint8)
+    rs = np.full((8, 4), 127, np.uint8)
+    exact = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
+    assert np.all(exact[:, 0] == 34.0625) and not exact[:, 1:].any()
+    data, scale = oracle.scaled_matmul_quantize(lhs, ls, rhs, rs, "e4m3fn", "e4m3fn")
+    assert scale[0, 0] == 124
+    assert np.all(data[:, 0] == 0x78) and not data[:, 1:].any()
+    assert oracle.narrow(np.float32([272.0, 272.5]), "e4m3fn").tolist() == [0x78, 0x79]
+
+
+def test_scaled_matmul_quantize_empty_k_and_shapes():
+    lhs = np.zeros((0, 32), np.uint8)
+    rhs = np.zeros((0, 16), np.uint8)
+    data, scale = oracle.scaled_matmul_quantize(lhs, np.zeros((0, 8), np.uint8), rhs, np.zeros((0, 4), np.uint8),
+                                                "e4m3fn", "e5m2")
+    assert data.shape == (8, 4) and not data.any()
+    assert scale[defcheck.scale_slot(np.arange(1))].tolist() == [[1]]   # an all-zero block has E8M0 1
+    with pytest.raises(ValueError):                                     # M % 8 != 0
+        oracle.scaled_matmul_quantize(np.zeros((8, 16), np.uint8), np.zeros((8, 4), np.uint8),
+                                      np.zeros((8, 16), np.uint8), np.zeros((8, 4), np.uint8), "e4m3fn", "e4m3fn")
