@@ -2,7 +2,7 @@
 """Throughput of the MX quantize on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op quantize|dequantize|matmul] [--res bf16|f32]
+                    [--op quantize|dequantize|matmul|matmul_quantize] [--res bf16|f32]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one full quantize of the workload tensor (one kernel launch: block
@@ -25,6 +25,10 @@ logical scale + result).
 operands (M = N = 8192, K = 4P = 8192 by default; ``--mm M N K``) in
 TFLOP/s against the matrix cores' dense FP8 peak.
 
+``--op matmul_quantize`` times the same product with its result quantized
+in the kernel's epilogue (format ``--out``, default e4m3fn), and reports the
+unfused pair (bf16 matmul, then quantize) on the same operands beside it.
+
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
 WRITE_SIZE readings into bytes.
@@ -46,6 +50,7 @@ if ROOT not in sys.path:
 METRIC = "MX quantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
 METRIC_DEQUANT = "MX dequantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
 METRIC_MATMUL = "MX scaled matmul TFLOP/s (fp32 accumulate), 1 MI355X"
+METRIC_MATMUL_QUANTIZE = "MX scaled matmul with quantized result TFLOP/s (fp32 accumulate), 1 MI355X"
 MFMA_FP8_PEAK_TFLOPS = 5000.0
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16-131072x8192-colscaled"
@@ -56,6 +61,9 @@ KERNEL_SOURCES = {
     "matmul": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
                "mx_microscaling_quantization_amd/csrc/mxq_matmul_kernels.hpp",
                "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
+    "matmul_quantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
+                        "mx_microscaling_quantization_amd/csrc/mxq_matmul_kernels.hpp",
+                        "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
     "dequantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
                    "mx_microscaling_quantization_amd/csrc/mxq_dequantize_kernels.hpp",
                    "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
@@ -160,9 +168,11 @@ def cpu_baseline_dequant(data, image, fmt: str, res: str, budget_s: float = 12.0
                       % (done_rows, P, done_rows, F, spent)}
 
 
-def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block: int = 16):
+def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block: int = 16,
+                        quantize_out: str | None = None):
     """The CPU oracle's scaled matmul (single thread) on block x block output
-    tiles along the diagonal until about budget_s seconds."""
+    tiles along the diagonal until about budget_s seconds; with quantize_out,
+    the oracle's matmul followed by its quantize of the tile."""
     import numpy as np
     import torch
 
@@ -179,7 +189,10 @@ def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block:
         hsl = sl[:, c0:c0 + block].contiguous().cpu().numpy()
         hsr = sr[:, c0:c0 + block].contiguous().cpu().numpy()
         t0 = time.perf_counter()
-        oracle.scaled_matmul(hl, hsl, hr, hsr, fmt)
+        if quantize_out:
+            oracle.scaled_matmul_quantize(hl, hsl, hr, hsr, fmt, quantize_out)
+        else:
+            oracle.scaled_matmul(hl, hsl, hr, hsr, fmt)
         spent += time.perf_counter() - t0
         done += 1
     flops = 2.0 * done * block * block * 4 * P
@@ -188,7 +201,33 @@ def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block:
                       % (done, block, block, 4 * P, spent)}
 
 
+def _time_steps(step, steps: int, warmup: int, stream):
+    """Per-launch HIP events on `stream` around each step, plus the span."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_begin.record(stream)
+    for k in range(steps):
+        starts[k].record(stream)
+        step()
+        ends[k].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    avg_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    return total_ms, avg_ms
+
+
 def bench_matmul(args) -> int:
+    """--op matmul: the scaled matmul (bf16 or f32 result). --op
+    matmul_quantize: the same product with its result quantized in the
+    kernel (format --out, default e4m3fn); the unfused pair (bf16 matmul,
+    then quantize) is timed on the same operands for comparison."""
     import torch
 
     import mx_microscaling_quantization_amd as mxq
@@ -198,6 +237,8 @@ def bench_matmul(args) -> int:
     M, N, K = args.mm
     P = K // 4
     fmt = "e4m3fn"
+    fused = args.op == "matmul_quantize"
+    qout = args.out or "e4m3fn"
     g = torch.Generator(device=dev)
     g.manual_seed(11)
     xl = torch.randn((P, 4 * M), generator=g, device=dev).to(torch.bfloat16)
@@ -205,44 +246,48 @@ def bench_matmul(args) -> int:
     dl, sl = mxq.quantize(xl, fmt)
     dr, sr = mxq.quantize(xr, fmt)
     del xl, xr
-    res_t = torch.bfloat16 if args.res == "bf16" else torch.float32
-    out = torch.empty((M, N), dtype=res_t, device=dev)
     stream = torch.cuda.current_stream(dev)
+    res_t = torch.bfloat16 if (args.res == "bf16" or fused) else torch.float32
+    out = torch.empty((M, N), dtype=res_t, device=dev)
+    compare = None
+    if fused:
+        qd = torch.empty(mxq.data_shape(M, N, qout), dtype=torch.uint8, device=dev)
+        qs = torch.zeros(mxq.scale_image_shape(M, N), dtype=torch.uint8, device=dev)
 
-    def step():
-        mxq.scaled_matmul(dl, sl, dr, sr, fmt, res_t, out=out, stream=stream)
+        def step():
+            mxq.scaled_matmul_quantize(dl, sl, dr, sr, fmt, qout, data_out=qd, scale_out=qs, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_begin.record(stream)
-    for k in range(args.steps):
-        starts[k].record(stream)
-        step()
-        ends[k].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    avg_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+        def unfused():
+            mxq.scaled_matmul(dl, sl, dr, sr, fmt, torch.bfloat16, out=out, stream=stream)
+            mxq.quantize(out, qout, data_out=qd, scale_out=qs, stream=stream)
+
+        u_total, u_avg = _time_steps(unfused, args.steps, args.warmup, stream)
+        compare = {"unfused_ms_per_step": round(u_total / args.steps, 5),
+                   "unfused": "scaled_matmul (bf16 result) then quantize",
+                   "result_bytes_not_written_or_read": 2 * 2 * M * N}
+    else:
+        def step():
+            mxq.scaled_matmul(dl, sl, dr, sr, fmt, res_t, out=out, stream=stream)
+
+    total_ms, avg_ms = _time_steps(step, args.steps, args.warmup, stream)
     flops = 2.0 * M * N * K
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
     result = {
-        "metric": METRIC_MATMUL, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic",
-        "config": {"workload": "%s-%dx%dx%d-scaled-matmul" % (fmt, M, N, K), "M": M, "N": N, "K": K,
-                   "out": args.res, "flops_per_step": flops},
+        "metric": METRIC_MATMUL_QUANTIZE if fused else METRIC_MATMUL, "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic",
+        "config": {"workload": "%s-%dx%dx%d-scaled-matmul%s" % (fmt, M, N, K, "-quantized-%s" % qout if fused else ""),
+                   "M": M, "N": N, "K": K, "out": qout if fused else args.res, "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel_avg_us": round(avg_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
+    if compare:
+        result["compare"] = compare
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_matmul(dl, sl, dr, sr, fmt)
+        result["cpu_baseline"] = cpu_baseline_matmul(dl, sl, dr, sr, fmt, quantize_out=qout if fused else None)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -274,7 +319,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--out", default=None, help="output format (default: the workload's first)")
-    ap.add_argument("--op", choices=("quantize", "dequantize", "matmul"), default="quantize")
+    ap.add_argument("--op", choices=("quantize", "dequantize", "matmul", "matmul_quantize"), default="quantize")
     ap.add_argument("--mm", type=int, nargs=3, default=(8192, 8192, 8192), metavar=("M", "N", "K"),
                     help="matmul sizes (M, N multiples of 4, K a multiple of 32)")
     ap.add_argument("--res", choices=("bf16", "f32"), default="bf16", help="dequantize result type")
@@ -300,7 +345,7 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.steps, args.warmup)
         return 0
-    if args.op == "matmul":
+    if args.op in ("matmul", "matmul_quantize"):
         return bench_matmul(args)
 
     dev = torch.device("cuda:0")

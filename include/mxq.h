@@ -213,6 +213,41 @@ size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype);
 int mxq_scaled_matmul(const void *lhs, const void *lhs_scale, const void *rhs, const void *rhs_scale, int64_t P,
                       int64_t M, int64_t N, int fmt, int res_dtype, unsigned flags, void *out, void *stream);
 
+/*
+ * mxq_scaled_matmul_quantize -- the scaled matmul with its result quantized
+ * in the same kernel (quantize-on-produce).
+ *
+ * "MX-FP8 Microscaling Legalization", The pipeline coupling: the quantize
+ * feeds the scaled matmul and the two compose by dataflow, so the next
+ * layer's quantize consumes the matmul's result. This call produces that
+ * quantized result directly, without writing the M x N result to memory.
+ *
+ * Reading: the bytes are exactly those of
+ *     mxq_scaled_matmul(..., MXQ_RES_BF16, ...) into a bf16 buffer R,
+ *     then mxq_quantize_ex(R, P = M, F = N, MXQ_IN_BF16, out_dtype, flags)
+ * -- the fp32 sum rounded to nearest-even bf16 (the matmul's BF16 result
+ * type, which the quantize takes), then quantized with 8-row x 4-column
+ * blocks of the M x N result, EMAX scale, saturating RNE, the FP4 lane
+ * order and the scale placement.
+ *
+ *   lhs ... rhs_scale, P, N, fmt   as for mxq_scaled_matmul.
+ *   M           multiple of 8 (the result's rows form row groups), else
+ *               MXQ_E_SHAPE_P8; M == 0 or N == 0 is an empty call.
+ *   out_dtype   enum mxq_out_dtype of the result's data.
+ *   flags       MXQ_FLAG_DENSE_SCALE: the operand scales are dense, and the
+ *               result scale is a dense [M/8, N/4] array (else an M x N/4
+ *               image, of which only the placed rows are written);
+ *               MXQ_FLAG_ALT_EMAX: the result's blocks use EMAX - 1.
+ *   data_out    mxq_data_bytes(M, N, out_dtype) bytes, 16-byte aligned.
+ *   scale_out   mxq_scale_bytes(M, N, flags) bytes, 16-byte aligned.
+ *   stream      hipStream_t of the current device (NULL = default).
+ * All pointers are device pointers. Returns MXQ_OK once enqueued, else an
+ * MXQ_E_* code with nothing enqueued.
+ */
+int mxq_scaled_matmul_quantize(const void *lhs, const void *lhs_scale, const void *rhs, const void *rhs_scale,
+                               int64_t P, int64_t M, int64_t N, int fmt, int out_dtype, unsigned flags,
+                               void *data_out, void *scale_out, void *stream);
+
 /* Human-readable message for a status code (static storage, never NULL). */
 const char *mxq_status_string(int status);
 

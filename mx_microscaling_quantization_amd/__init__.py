@@ -70,6 +70,10 @@ def load():
         lib.mxq_scaled_matmul.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_int64,
                                           c.c_int64, c.c_int, c.c_int, c.c_uint, c.c_void_p, c.c_void_p]
         lib.mxq_scaled_matmul.restype = c.c_int
+        lib.mxq_scaled_matmul_quantize.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64,
+                                                   c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_uint, c.c_void_p,
+                                                   c.c_void_p, c.c_void_p]
+        lib.mxq_scaled_matmul_quantize.restype = c.c_int
         lib.mxq_scale_bytes.argtypes = [c.c_int64, c.c_int64, c.c_uint]
         lib.mxq_scale_bytes.restype = c.c_size_t
         lib.mxq_data_bytes.argtypes = [c.c_int64, c.c_int64, c.c_int]
@@ -256,3 +260,53 @@ def scaled_matmul(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor,
                                      code, RES_DTYPES[res_dtype], FLAG_DENSE_SCALE if dense_scale else 0,
                                      out.data_ptr(), stream.cuda_stream))
     return out
+
+
+def _check_operands(lhs, lhs_scale, rhs, rhs_scale, dense_scale):
+    for t in (lhs, lhs_scale, rhs, rhs_scale):
+        if t.dim() != 2 or t.dtype != torch.uint8 or not t.is_contiguous() or t.device != lhs.device or not t.is_cuda:
+            raise ValueError("operands must be contiguous 2-D uint8 device tensors on one device")
+    P = lhs.shape[0]
+    M, N = lhs.shape[1] // 4, rhs.shape[1] // 4
+    if rhs.shape[0] != P or lhs.shape[1] % 4 or rhs.shape[1] % 4:
+        raise ValueError("lhs [P, 4M] and rhs [P, 4N] must share P")
+    if tuple(lhs_scale.shape) != scale_image_shape(P, 4 * M, dense_scale) or \
+            tuple(rhs_scale.shape) != scale_image_shape(P, 4 * N, dense_scale):
+        raise ValueError("scale shapes do not match the operands")
+    return P, M, N
+
+
+def scaled_matmul_quantize(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor, rhs_scale: torch.Tensor,
+                           fmt: str = "e4m3fn", out_dtype: str = "e4m3fn", data_out: torch.Tensor | None = None,
+                           scale_out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
+                           alt_emax: bool = False, dense_scale: bool = False):
+    """The scaled matmul with its [M, N] result quantized in the same kernel.
+
+    Operands as for :func:`scaled_matmul`. Returns ``(data, scale)`` -- the
+    bytes :func:`quantize` would write for the bfloat16 result of
+    :func:`scaled_matmul` (P = M rows, F = N columns, format ``out_dtype``),
+    without that result ever being stored. ``dense_scale`` applies to the
+    operand scales and the result scale; ``alt_emax`` to the result.
+    """
+    lib = load()
+    code = _out_code(fmt)
+    out_code = _out_code(out_dtype)
+    P, M, N = _check_operands(lhs, lhs_scale, rhs, rhs_scale, dense_scale)
+    flags = (FLAG_ALT_EMAX if alt_emax else 0) | (FLAG_DENSE_SCALE if dense_scale else 0)
+    if M % 8:
+        raise MXQError(3, "the result's rows M = %d must be a multiple of 8" % M)
+    if data_out is None:
+        data_out = torch.empty(data_shape(M, N, out_dtype), dtype=torch.uint8, device=lhs.device)
+    if scale_out is None:
+        scale_out = torch.empty(scale_image_shape(M, N, dense_scale), dtype=torch.uint8, device=lhs.device)
+    for name, t, nbytes in (("data_out", data_out, lib.mxq_data_bytes(M, N, out_code)),
+                            ("scale_out", scale_out, lib.mxq_scale_bytes(M, N, flags))):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.device != lhs.device or t.numel() != nbytes:
+            raise ValueError("%s must be a contiguous uint8 tensor of %d bytes on %s" % (name, nbytes, lhs.device))
+    if stream is None:
+        stream = torch.cuda.current_stream(lhs.device)
+    with torch.cuda.device(lhs.device):
+        _check(lib.mxq_scaled_matmul_quantize(lhs.data_ptr(), lhs_scale.data_ptr(), rhs.data_ptr(),
+                                              rhs_scale.data_ptr(), P, M, N, code, out_code, flags,
+                                              data_out.data_ptr(), scale_out.data_ptr(), stream.cuda_stream))
+    return data_out, scale_out

@@ -165,11 +165,92 @@ __device__ __forceinline__ i32x8_t mm_operand(const uint8_t *tile, uint32_t lo, 
     return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-template <int FMT, int RES>
+// What the kernel does with its fp32 sums: store them, store them rounded
+// to bf16, or quantize them (rounded to bf16) into MX data + E8M0 scales of
+// format EPI - kEpiMx.
+enum { kEpiF32 = 0, kEpiBF16 = 1, kEpiMx = 2 };
+
+// fp32 -> bf16 bits, round to nearest even; a NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t mm_bf16_bits(float v)
+{
+    const uint32_t bits = __float_as_uint(v);
+    if ((bits & 0x7FFFFFFFu) > 0x7F800000u)
+        return (bits >> 16) | 0x40u;
+    return (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+}
+
+// Quantize-on-produce ("MX-FP8 Microscaling Legalization", The pipeline
+// coupling): the wave's 128 x 128 sums, rounded to bf16, are quantized as the
+// quantize kernel would quantize that bf16 tensor -- 8-row x 4-column blocks
+// of the M x N result, the same conversions and special-code pass -- and
+// written as MX data (pitch N, or N / 2 for FP4) and E8M0 bytes.
+//
+// Lane (i, g) holds column 16 b + i, rows 4 g .. 4 g + 3 of sub-tile (a, b).
+// Within each quad of lanes (4 consecutive columns) the bf16 values are
+// transposed so that lane k of the quad holds row 4 g + k, columns 4 q ..
+// 4 q + 3: one x4 container. A block (rows 8 h .. 8 h + 7, the quad's
+// columns) is then the quad's 4 lanes in lane groups 2 h and 2 h + 1, and
+// its maximum is a reduction over lanes xor 1, xor 2 and xor 16. Every lane
+// runs the shuffles (full EXEC); only the stores are predicated.
+template <int OUT>
+__device__ __forceinline__ void mm_quantize_epilogue(const f32x4_t (&acc)[kMmSub][kMmSub], uint32_t row0,
+                                                     uint32_t col0, uint32_t M, uint32_t N, uint32_t lane,
+                                                     uint8_t *__restrict__ data, uint8_t *__restrict__ scale,
+                                                     int emax_bias, uint32_t dense)
+{
+    const uint32_t i = lane & 15u, g = lane >> 4, k = lane & 3u, quad = lane & ~3u;
+#pragma unroll
+    for (int a = 0; a < kMmSub; a++)
+#pragma unroll
+        for (int b = 0; b < kMmSub; b++) {
+            const uint32_t c01 = mm_bf16_bits(acc[a][b][0]) | mm_bf16_bits(acc[a][b][1]) << 16;
+            const uint32_t c23 = mm_bf16_bits(acc[a][b][2]) | mm_bf16_bits(acc[a][b][3]) << 16;
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t d01 = (uint32_t)__shfl((int)c01, (int)(quad | j));
+                const uint32_t d23 = (uint32_t)__shfl((int)c23, (int)(quad | j));
+                h[j] = ((k & 2u) ? d23 : d01) >> (16u * (k & 1u)) & 0xFFFFu;
+            }
+            uint32_t w[2] = {h[0] | h[1] << 16, h[2] | h[3] << 16};
+
+            const uint32_t m2 = pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu);
+            uint32_t mag = max(m2 & 0xFFFFu, m2 >> 16);
+            mag = max(mag, (uint32_t)__shfl_xor((int)mag, 1));
+            mag = max(mag, (uint32_t)__shfl_xor((int)mag, 2));
+            mag = max(mag, (uint32_t)__shfl_xor((int)mag, 16));
+            uint32_t e[1] = {block_e8m0<kInBF16>(mag, emax_bias)};
+            const float sc = e8m0_to_scale(e[0]);
+            const bool special = mag > InfBits<kInBF16>::value || e[0] == 254u;
+
+            const uint32_t row = row0 + 16u * a + 4u * g + k;
+            const uint32_t col = col0 + 16u * b + 4u * (i >> 2);
+            uint32_t out[1];
+            if constexpr (OUT == kOutE2M1)
+                out[0] = fp4_container<kInBF16, 0>(0u, w[0], w[1], sc);
+            else
+                out[0] = fp8x4<kInBF16, OUT>(w[0], w[1], sc);
+            if (special)
+                fix_special_codes<kInBF16, OUT, 1>(w, e, out);
+            if (row < M && col < N) {
+                if constexpr (OUT == kOutE2M1)
+                    *reinterpret_cast<uint16_t *>(data + ((uint64_t)row * N + col) / 2) = (uint16_t)out[0];
+                else
+                    *reinterpret_cast<uint32_t *>(data + (uint64_t)row * N + col) = out[0];
+                if (k == 0 && (g & 1u) == 0) {   // the block's first row writes its E8M0
+                    const uint32_t grp = row / 8;
+                    const uint64_t slot = dense ? grp : (grp & 3u) + 32ull * (grp >> 2);
+                    scale[slot * (N / 4) + col / 4] = (uint8_t)e[0];
+                }
+            }
+        }
+}
+
+template <int FMT, int EPI>
 __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
     const uint8_t *__restrict__ lhs, const uint8_t *__restrict__ lhs_scale, const uint8_t *__restrict__ rhs,
     const uint8_t *__restrict__ rhs_scale, uint32_t P, uint32_t M, uint32_t N, uint32_t tiles_n, uint32_t dense,
-    void *__restrict__ out)
+    void *__restrict__ out, uint8_t *__restrict__ out_scale, int emax_bias)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMmStageBytes];
     constexpr int F = MfmaFmt<FMT>::value;
@@ -312,6 +393,11 @@ __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
         }
     }
 
+    if constexpr (EPI >= kEpiMx) {
+        mm_quantize_epilogue<EPI - kEpiMx>(acc, m0 + wm, n0 + wn, M, N, lane, reinterpret_cast<uint8_t *>(out),
+                                           out_scale, emax_bias, dense);
+        return;
+    }
     // result register r of lane (i, g) in sub-tile (a, b) is
     // out[m0 + wm + 16a + 4g + r][n0 + wn + 16b + i]
 #pragma unroll
@@ -324,17 +410,10 @@ __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
                 const uint32_t n = n0 + wn + 16u * b + i;
                 if (m < M && n < N) {
                     const uint64_t o = (uint64_t)m * N + n;
-                    if constexpr (RES == 0) {
+                    if constexpr (EPI == kEpiF32)
                         reinterpret_cast<float *>(out)[o] = acc[a][b][r];
-                    } else {
-                        const uint32_t bits = __float_as_uint(acc[a][b][r]);
-                        uint32_t rb;
-                        if ((bits & 0x7FFFFFFFu) > 0x7F800000u)
-                            rb = (bits >> 16) | 0x40u;
-                        else
-                            rb = (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
-                        reinterpret_cast<uint16_t *>(out)[o] = (uint16_t)rb;
-                    }
+                    else
+                        reinterpret_cast<uint16_t *>(out)[o] = (uint16_t)mm_bf16_bits(acc[a][b][r]);
                 }
             }
 }

@@ -191,6 +191,30 @@ def test_scaled_matmul_validation_errors_before_launch():
     assert mm(32, 4, 4, ptrs=(g, g, g, g + 4, g)) == e["MXQ_E_ALIGN"]
 
 
+def test_scaled_matmul_quantize_validation_errors_before_launch():
+    e = _header_enums()
+    lib = mxq.load()
+    g = 4096
+
+    def mq(P, M, N, fmt=0, out=0, flags=0, ptrs=(g, g, g, g, g, g)):
+        a, b, c, d, o, s = ptrs
+        return lib.mxq_scaled_matmul_quantize(a, b, c, d, P, M, N, fmt, out, flags, o, s, None)
+
+    assert mq(32, 8, 4, fmt=2) == e["MXQ_E_OUT_DTYPE"]          # operands are FP8 only
+    assert mq(32, 8, 4, out=3) == e["MXQ_E_OUT_DTYPE"]
+    assert mq(32, 8, 4, flags=4) == e["MXQ_E_FLAGS"]
+    assert mq(12, 8, 4) == e["MXQ_E_SHAPE_P8"]
+    assert mq(32, 4, 4) == e["MXQ_E_SHAPE_P8"]                  # result rows form 8-row groups
+    assert mq(32, 8, 6) == e["MXQ_E_SHAPE_F4"]
+    assert mq(32, e["MXQ_MATMUL_MAX_COLS"] + 8, 4) == e["MXQ_E_OVERFLOW"]
+    assert mq(32, 0, 4, ptrs=(None,) * 6) == 0
+    assert mq(32, 8, 4, ptrs=(g, g, None, g, g, g)) == e["MXQ_E_NULL"]
+    assert mq(32, 8, 4, ptrs=(g, g, g, g, g, None)) == e["MXQ_E_NULL"]
+    assert mq(32, 8, 4, ptrs=(g, g, g, g, g + 8, g)) == e["MXQ_E_ALIGN"]
+    for flags in (0, 1, 2, 3):                                   # every documented flag combination passes validation
+        assert mq(32, 8, 4, flags=flags, ptrs=(None,) * 6) == e["MXQ_E_NULL"]
+
+
 def test_empty_tensors_are_noops():
     for P, F in ((0, 8), (8, 0), (0, 0)):
         for out in range(3):
