@@ -64,6 +64,9 @@ def _load():
         lib.mxq_oracle_scaled_matmul_quantize.argtypes = [P_u8, P_u8, P_u8, P_u8, c.c_int64, c.c_int64, c.c_int64,
                                                           c.c_int, c.c_int, c.c_int, c.c_int, P_u8, P_u8]
         lib.mxq_oracle_scaled_matmul_quantize.restype = c.c_int
+        lib.mxq_oracle_quantize_axis.argtypes = [P_u16, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_int,
+                                                 c.c_int, P_u8, P_u8]
+        lib.mxq_oracle_quantize_axis.restype = c.c_int
         lib.mxq_oracle_widen_array.argtypes = [P_u16, c.c_int64, c.c_int, P_f32]
         lib.mxq_oracle_narrow_array.argtypes = [P_f32, c.c_int64, c.c_int, P_u8]
         lib.mxq_oracle_prescale_array.argtypes = [P_f32, P_u8, c.c_int64, P_f32]
@@ -125,6 +128,30 @@ def quantize(x: np.ndarray, in_dtype: str, out_dtype: str, alt_emax: bool = Fals
     if rc != 0:
         raise ValueError("oracle quantize rejected the call (status %d)" % rc)
     return data, image
+
+
+def quantize_axis(x: np.ndarray, in_dtype: str, out_dtype: str, dim: int, alt_emax: bool = False,
+                  layout: str = "image"):
+    """Quantize a row-major [R, C] array of bf16/f16 bit patterns with
+    32-element blocks along axis ``dim`` (-1: along rows, K = C; -2: down
+    columns, K = R). Returns ``(data, scale)`` in the partition-major layout
+    :func:`quantize` produces for the [K/4, 4*O] view (O the other extent)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    R, C = x.shape
+    d = dim + 2 if dim < 0 else dim
+    K, O = (C, R) if d == 1 else (R, C)
+    if d not in (0, 1) or K % 32:
+        raise ValueError("dim must be -1 or -2 and the block axis a multiple of 32")
+    P, F = K // 4, 4 * O
+    data = np.zeros(data_shape(P, F, out_dtype), dtype=np.uint8)
+    scale = np.zeros(scale_shape(P, F, layout), dtype=np.uint8)
+    rc = lib.mxq_oracle_quantize_axis(_ptr(x, ctypes.c_uint16), R, C, IN_CODES[in_dtype], OUT_CODES[out_dtype], dim,
+                                      int(bool(alt_emax)), LAYOUTS[layout], _ptr(data, ctypes.c_uint8),
+                                      _ptr(scale, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle quantize_axis rejected the call (status %d)" % rc)
+    return data, scale
 
 
 RES_CODES = {"f32": 0, "bf16": 1}

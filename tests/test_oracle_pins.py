@@ -611,3 +611,86 @@ def test_scaled_matmul_quantize_empty_k_and_shapes():
     with pytest.raises(ValueError):                                     # M % 8 != 0
         oracle.scaled_matmul_quantize(np.zeros((8, 16), np.uint8), np.zeros((8, 4), np.uint8),
                                       np.zeros((8, 16), np.uint8), np.zeros((8, 4), np.uint8), "e4m3fn", "e4m3fn")
+
+
+# ------------------------------------------------------- quantize along an axis
+
+def _device_view(x: np.ndarray, dim: int) -> np.ndarray:
+    """numpy re-layout of a row-major [R, C] tensor into the [K/4, 4*O]
+    partition-major view: element (p, 4o + j) = block-axis element 4p + j
+    at other-axis index o."""
+    d = dim + 2 if dim < 0 else dim
+    if d == 1:                                   # blocks along rows: X[o][k]
+        O, K = x.shape
+        return x.reshape(O, K // 4, 4).transpose(1, 0, 2).reshape(K // 4, 4 * O)
+    K, O = x.shape                               # blocks down columns: W[k][o]
+    return x.reshape(K // 4, 4, O).transpose(0, 2, 1).reshape(K // 4, 4 * O)
+
+
+@pytest.mark.parametrize("in_dtype,fmt", [("bf16", "e4m3fn"), ("f16", "e5m2"), ("bf16", "e2m1")])
+@pytest.mark.parametrize("dim,R,C", [(-2, 32, 4), (0, 64, 36), (-2, 96, 64), (-1, 96, 64), (1, 4, 32),
+                                     (-1, 13, 96)])
+def test_quantize_axis_equals_definition(dim, in_dtype, fmt, R, C):
+    x = workloads.random_bits(R, C, in_dtype, seed=R * 7 + C + dim, specials=True)
+    for alt, layout in ((False, "image"), (True, "dense")):
+        want = defcheck.quantize(_device_view(x, dim), in_dtype, fmt, alt=alt, layout=layout)
+        got = oracle.quantize_axis(x, in_dtype, fmt, dim, alt_emax=alt, layout=layout)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_quantize_axis_hand_worked_positions():
+    """One nonzero element 1.0 at block-axis index 5, other-axis index 1:
+    block max 1.0 -> E8M0 127 - 8 = 119 -> prescale 2^8 -> 256 = 0x78, at
+    device row 5 // 4 = 1, column 4 * 1 + 5 % 4 = 5; every other code 0."""
+    one = np.uint16(0x3F80)                      # bf16 1.0
+    w = np.zeros((32, 2), np.uint16)             # W[k][n], dim -2
+    w[5, 1] = one
+    x = np.zeros((2, 32), np.uint16)             # X[m][k], dim -1
+    x[1, 5] = one
+    for t, dim in ((w, -2), (x, -1)):
+        data, scale = oracle.quantize_axis(t, "bf16", "e4m3fn", dim)
+        assert data.shape == (8, 8)
+        assert data[1, 5] == 0x78 and np.count_nonzero(data) == 1
+        assert scale[0].tolist() == [1, 119]     # block of column 0 is all zero -> E8M0 1
+
+
+@pytest.mark.parametrize("fmt", ("e4m3fn", "e5m2", "e2m1"))
+def test_quantize_axis_grid_values_round_trip_through_the_layout(fmt):
+    """Inputs on the format's grid at every block scale round-trip exactly:
+    the dequantized device view equals numpy's re-layout of the input."""
+    rng = np.random.default_rng(12)
+    grid = {"e4m3fn": [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0], "e5m2": [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0],
+            "e2m1": [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0]}[fmt]
+    for dim, shape in ((-1, (24, 64)), (-2, (96, 20))):
+        v = rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        v = (v * np.ldexp(1.0, rng.integers(-20, 20, size=(1, shape[1]) if dim == -2 else (shape[0], 1)))
+             ).astype(np.float32)
+        bits = workloads.f32_to_bf16_bits(v)
+        data, scale = oracle.quantize_axis(bits, "bf16", fmt, dim)
+        P, F = _device_view(bits, dim).shape
+        back = oracle.dequantize(data, scale, P, F, fmt, "f32")
+        assert np.array_equal(back, _device_view(v, dim))
+
+
+def test_quantize_axis_feeds_the_matmul_as_x_times_w():
+    """Small integers are exact in e4m3fn at E8M0 127..: quantizing X [M, K]
+    along its rows and W [K, N] down its columns gives operands whose scaled
+    matmul is X @ W exactly -- the axis layout and the matmul's operand
+    reading agree."""
+    rng = np.random.default_rng(13)
+    M, K, N = 12, 64, 20
+    X = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    W = rng.integers(-4, 5, size=(K, N)).astype(np.float32)
+    dl, sl = oracle.quantize_axis(workloads.f32_to_bf16_bits(X), "bf16", "e4m3fn", -1)
+    dr, sr = oracle.quantize_axis(workloads.f32_to_bf16_bits(W), "bf16", "e4m3fn", -2)
+    got = oracle.scaled_matmul(dl, sl, dr, sr, "e4m3fn")
+    assert np.array_equal(got, X.astype(np.float64) @ W.astype(np.float64))
+
+
+def test_quantize_axis_rejects_bad_axes():
+    x = np.zeros((32, 32), np.uint16)
+    for bad in (2, -3):
+        with pytest.raises(ValueError):
+            oracle.quantize_axis(x, "bf16", "e4m3fn", bad)
+    with pytest.raises(ValueError):
+        oracle.quantize_axis(np.zeros((32, 20), np.uint16), "bf16", "e4m3fn", -1)   # K = 20
