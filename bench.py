@@ -2,7 +2,8 @@
 """Throughput of the MX quantize on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op quantize|dequantize|matmul|matmul_quantize] [--res bf16|f32]
+                    [--op quantize|dequantize|matmul|matmul_quantize|quantize_axis]
+                    [--dim -1|-2] [--res bf16|f32]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one full quantize of the workload tensor (one kernel launch: block
@@ -24,6 +25,11 @@ logical scale + result).
 ``--op matmul`` times the block-scaled matmul of two quantized e4m3fn
 operands (M = N = 8192, K = 4P = 8192 by default; ``--mm M N K``) in
 TFLOP/s against the matrix cores' dense FP8 peak.
+
+``--op quantize_axis [--dim -1|-2]`` times the quantize of the same input as
+a plain row-major tensor with its blocks along rows (-1) or down columns
+(-2), written in the partition-major layout the matmul reads (same bytes
+per step as the quantize).
 
 ``--op matmul_quantize`` times the same product with its result quantized
 in the kernel's epilogue (format ``--out``, default e4m3fn), and reports the
@@ -49,25 +55,26 @@ if ROOT not in sys.path:
 
 METRIC = "MX quantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
 METRIC_DEQUANT = "MX dequantize GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
+METRIC_AXIS = "MX quantize along a tensor axis GB/s (in+out bytes) and % of HBM peak, 1 MI355X"
 METRIC_MATMUL = "MX scaled matmul TFLOP/s (fp32 accumulate), 1 MI355X"
 METRIC_MATMUL_QUANTIZE = "MX scaled matmul with quantized result TFLOP/s (fp32 accumulate), 1 MI355X"
 MFMA_FP8_PEAK_TFLOPS = 5000.0
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16-131072x8192-colscaled"
 PROFILES = os.path.join(ROOT, "profiles")
+_CSRC = "mx_microscaling_quantization_amd/csrc/"
+# What determines each op's kernel and launch: its kernel header(s), its
+# launch file and the shared host helpers.
 KERNEL_SOURCES = {
-    "quantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
-                 "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
-    "matmul": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
-               "mx_microscaling_quantization_amd/csrc/mxq_matmul_kernels.hpp",
-               "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
-    "matmul_quantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
-                        "mx_microscaling_quantization_amd/csrc/mxq_matmul_kernels.hpp",
-                        "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
-    "dequantize": ["mx_microscaling_quantization_amd/csrc/mxq_quantize_kernels.hpp",
-                   "mx_microscaling_quantization_amd/csrc/mxq_dequantize_kernels.hpp",
-                   "mx_microscaling_quantization_amd/csrc/mxq_api.hip"],
+    "quantize": [_CSRC + f for f in ("mxq_quantize_kernels.hpp", "mxq_quantize_api.hip", "mxq_host.hpp")],
+    "dequantize": [_CSRC + f for f in ("mxq_quantize_kernels.hpp", "mxq_dequantize_kernels.hpp",
+                                       "mxq_dequantize_api.hip", "mxq_host.hpp")],
+    "matmul": [_CSRC + f for f in ("mxq_quantize_kernels.hpp", "mxq_matmul_kernels.hpp", "mxq_matmul_api.hip",
+                                   "mxq_host.hpp")],
+    "quantize_axis": [_CSRC + f for f in ("mxq_quantize_kernels.hpp", "mxq_axis_kernels.hpp", "mxq_axis_api.hip",
+                                          "mxq_host.hpp")],
 }
+KERNEL_SOURCES["matmul_quantize"] = KERNEL_SOURCES["matmul"]
 
 
 def algorithmic_bytes(P: int, F: int, out: str) -> int:
@@ -122,9 +129,10 @@ def make_input(workload: str, device):
     return xt, spec
 
 
-def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows: int = 4096):
+def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows: int = 4096, dim: int | None = None):
     """The CPU oracle (single thread, as it stands) on leading row slabs of
-    the same input until about budget_s seconds of oracle time."""
+    the same input until about budget_s seconds of oracle time (with dim,
+    its quantize along that axis; slabs stay multiples of 32 rows)."""
     import numpy as np
     import torch
 
@@ -137,7 +145,10 @@ def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows:
         rows = min(slab_rows, P - done_rows)
         x = xt[done_rows:done_rows + rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        oracle.quantize(x, in_dtype, out)
+        if dim is None:
+            oracle.quantize(x, in_dtype, out)
+        else:
+            oracle.quantize_axis(x, in_dtype, out, dim)
         spent += time.perf_counter() - t0
         done_rows += rows
     nbytes = algorithmic_bytes(done_rows, F, out)
@@ -319,7 +330,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--out", default=None, help="output format (default: the workload's first)")
-    ap.add_argument("--op", choices=("quantize", "dequantize", "matmul", "matmul_quantize"), default="quantize")
+    ap.add_argument("--op", choices=("quantize", "dequantize", "matmul", "matmul_quantize", "quantize_axis"),
+                    default="quantize")
+    ap.add_argument("--dim", type=int, choices=(-1, -2), default=-2,
+                    help="quantize_axis: block axis of the row-major input (-1 along rows, -2 down columns)")
     ap.add_argument("--mm", type=int, nargs=3, default=(8192, 8192, 8192), metavar=("M", "N", "K"),
                     help="matmul sizes (M, N multiples of 4, K a multiple of 32)")
     ap.add_argument("--res", choices=("bf16", "f32"), default="bf16", help="dequantize result type")
@@ -360,6 +374,14 @@ def main() -> int:
         def step():
             mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
         nbytes = algorithmic_bytes(P, F, out)
+    elif args.op == "quantize_axis":
+        VP, VF = mxq.axis_view_shape(P, F, args.dim)
+        data = torch.empty(mxq.data_shape(VP, VF, out), dtype=torch.uint8, device=dev)
+        image = torch.zeros(mxq.scale_image_shape(VP, VF), dtype=torch.uint8, device=dev)
+
+        def step():
+            mxq.quantize_axis(xt, out, args.dim, data_out=data, scale_out=image, stream=stream)
+        nbytes = algorithmic_bytes(P, F, out)
     else:
         mxq.quantize(xt, out, data_out=data, scale_out=image, stream=stream)
         torch.cuda.synchronize()
@@ -394,16 +416,21 @@ def main() -> int:
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
     if args.op == "quantize":
         traffic = recorded_traffic(args.workload, out)
+    elif args.op == "quantize_axis":
+        traffic = recorded_traffic(args.workload, out, "quantize_axis", "dim%d" % args.dim)
     else:
         traffic = recorded_traffic(args.workload, out, "dequantize", args.res)
 
     config = {"workload": args.workload, "P": P, "F": F, "in": spec["in_dtype"], "out": out,
               "bytes_per_step": nbytes, "elements_per_step": P * F}
+    if args.op == "quantize_axis":
+        config = {"workload": "%s-axis%d" % (args.workload, args.dim), "R": P, "C": F, "dim": args.dim,
+                  "in": spec["in_dtype"], "out": out, "bytes_per_step": nbytes, "elements_per_step": P * F}
     if args.op == "dequantize":
         config = {"workload": args.workload + "-dequantize", "P": P, "F": F, "in": out, "out": args.res,
                   "bytes_per_step": nbytes, "elements_per_step": P * F}
     result = {
-        "metric": METRIC if args.op == "quantize" else METRIC_DEQUANT,
+        "metric": {"quantize": METRIC, "quantize_axis": METRIC_AXIS}.get(args.op, METRIC_DEQUANT),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -413,7 +440,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": spec["in_dtype"] if args.op == "quantize" else out,
+        "dtype": out if args.op == "dequantize" else spec["in_dtype"],
         "data": "synthetic",
         "config": config,
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -426,6 +453,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         if args.op == "quantize":
             result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"])
+        elif args.op == "quantize_axis":
+            result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"], dim=args.dim)
         else:
             result["cpu_baseline"] = cpu_baseline_dequant(data, image, out, args.res)
     print(json.dumps(result), flush=True)

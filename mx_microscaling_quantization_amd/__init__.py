@@ -74,6 +74,9 @@ def load():
                                                    c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_uint, c.c_void_p,
                                                    c.c_void_p, c.c_void_p]
         lib.mxq_scaled_matmul_quantize.restype = c.c_int
+        lib.mxq_quantize_axis.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int, c.c_int, c.c_int, c.c_uint,
+                                          c.c_void_p, c.c_void_p, c.c_void_p]
+        lib.mxq_quantize_axis.restype = c.c_int
         lib.mxq_scale_bytes.argtypes = [c.c_int64, c.c_int64, c.c_uint]
         lib.mxq_scale_bytes.restype = c.c_size_t
         lib.mxq_data_bytes.argtypes = [c.c_int64, c.c_int64, c.c_int]
@@ -309,4 +312,50 @@ def scaled_matmul_quantize(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torc
         _check(lib.mxq_scaled_matmul_quantize(lhs.data_ptr(), lhs_scale.data_ptr(), rhs.data_ptr(),
                                               rhs_scale.data_ptr(), P, M, N, code, out_code, flags,
                                               data_out.data_ptr(), scale_out.data_ptr(), stream.cuda_stream))
+    return data_out, scale_out
+
+
+def axis_view_shape(R: int, C: int, dim: int):
+    """(P, F) of the partition-major view that :func:`quantize_axis` writes
+    for an R x C tensor: (K/4, 4*O) with K the block axis' extent."""
+    d = dim + 2 if dim < 0 else dim
+    if d not in (0, 1):
+        raise MXQError(11, "quantize axis must be -1 or -2 (or 1, 0), got %r" % dim)
+    K, O = (C, R) if d == 1 else (R, C)
+    return K // 4, 4 * O
+
+
+def quantize_axis(x: torch.Tensor, out_dtype: str = "e4m3fn", dim: int = -1, data_out: torch.Tensor | None = None,
+                  scale_out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None,
+                  alt_emax: bool = False, dense_scale: bool = False):
+    """Quantize a row-major [R, C] bf16/f16 device tensor with its 32-element
+    blocks along ``dim`` (-1: along each row, -2: down each column).
+
+    Returns ``(data, scale)`` in the layout :func:`quantize` produces for the
+    partition-major [K/4, 4*O] view (K the block axis' extent, O the other):
+    the operand layout of :func:`scaled_matmul`. Activations X [M, K] with
+    ``dim=-1`` and weights W [K, N] with ``dim=-2`` make it compute X @ W.
+    """
+    lib = load()
+    code = _out_code(out_dtype)
+    if x.dtype not in IN_DTYPES:
+        raise MXQError(1, "input must be bfloat16 or float16, got %s" % x.dtype)
+    if x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D device tensor [R, C]")
+    R, C = x.shape
+    P, F = axis_view_shape(R, C, dim)
+    flags = (FLAG_ALT_EMAX if alt_emax else 0) | (FLAG_DENSE_SCALE if dense_scale else 0)
+    if data_out is None:
+        data_out = torch.empty(data_shape(P, F, out_dtype), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty(scale_image_shape(P, F, dense_scale), dtype=torch.uint8, device=x.device)
+    for name, t, nbytes in (("data_out", data_out, lib.mxq_data_bytes(P, F, code)),
+                            ("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags))):
+        if t.device != x.device or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+            raise ValueError("%s must be a contiguous buffer of >= %d bytes on %s" % (name, nbytes, x.device))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        _check(lib.mxq_quantize_axis(x.data_ptr(), R, C, IN_DTYPES[x.dtype], code, dim, flags, data_out.data_ptr(),
+                                     scale_out.data_ptr(), stream.cuda_stream))
     return data_out, scale_out

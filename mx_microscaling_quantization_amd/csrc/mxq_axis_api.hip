@@ -1,0 +1,136 @@
+// mxq_axis_api.hip -- mxq_quantize_axis: validation, the [K/4, 4*O] view's
+// geometry, and dispatch to quantize_down_kernel (dim -2) or
+// quantize_along_kernel (dim -1) on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxq.h"
+#include "mxq_host.hpp"
+#include "mxq_axis_kernels.hpp"
+
+namespace {
+
+using mxq_host::check_shape;
+using mxq_host::emax_of;
+using mxq_host::kMaxF;
+using mxq_host::kMaxWorkgroups;
+
+typedef void (*down_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, int, uint32_t);
+typedef void (*along_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint64_t, uint32_t, int, uint32_t);
+
+template <int IN, int OUT> down_kernel_fn down_pick_nb(int nb)
+{
+    switch (nb) {
+    case 4: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 4>;
+    case 2: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 2>;
+    default: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 1>;
+    }
+}
+
+template <int IN, int OUT> along_kernel_fn along_pick_gb(int gb)
+{
+    return gb == 2 ? (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT, 2>
+                   : (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT, 1>;
+}
+
+template <int IN> void axis_pick(int out_dtype, int down, int width, down_kernel_fn *d, along_kernel_fn *a)
+{
+    switch (out_dtype) {
+    case MXQ_OUT_E4M3FN:
+        *d = down ? down_pick_nb<IN, mxq::kOutE4M3FN>(width) : nullptr;
+        *a = down ? nullptr : along_pick_gb<IN, mxq::kOutE4M3FN>(width);
+        break;
+    case MXQ_OUT_E5M2:
+        *d = down ? down_pick_nb<IN, mxq::kOutE5M2>(width) : nullptr;
+        *a = down ? nullptr : along_pick_gb<IN, mxq::kOutE5M2>(width);
+        break;
+    default:
+        *d = down ? down_pick_nb<IN, mxq::kOutE2M1>(width) : nullptr;
+        *a = down ? nullptr : along_pick_gb<IN, mxq::kOutE2M1>(width);
+        break;
+    }
+}
+
+} // namespace
+
+extern "C" {
+
+int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int out_dtype, int dim, unsigned flags,
+                      void *data_out, void *scale_out, void *stream)
+{
+    if (in_dtype != MXQ_IN_BF16 && in_dtype != MXQ_IN_F16)
+        return MXQ_E_IN_DTYPE;
+    if (out_dtype != MXQ_OUT_E4M3FN && out_dtype != MXQ_OUT_E5M2 && out_dtype != MXQ_OUT_E2M1)
+        return MXQ_E_OUT_DTYPE;
+    if (flags & ~(unsigned)(MXQ_FLAG_ALT_EMAX | MXQ_FLAG_DENSE_SCALE))
+        return MXQ_E_FLAGS;
+    if (dim < 0)
+        dim += 2; // rank 2: -1 -> 1 (last), -2 -> 0 (second-to-last)
+    if (dim != 0 && dim != 1)
+        return MXQ_E_DIM;
+    if (R < 0 || C < 0)
+        return MXQ_E_SHAPE_F4;
+    const int down = dim == 0;
+    const int64_t K = down ? R : C, O = down ? C : R;
+    if (K % 32 != 0)
+        return MXQ_E_SHAPE_P8;
+    if (O > kMaxF / 4)
+        return MXQ_E_OVERFLOW;
+    int rc = check_shape(K / 4, 4 * O); // the [K/4, 4*O] view's limits
+    if (rc != MXQ_OK)
+        return rc;
+    if (R == 0 || C == 0)
+        return MXQ_OK;
+    if (!in || !data_out || !scale_out)
+        return MXQ_E_NULL;
+    if (((uintptr_t)in | (uintptr_t)data_out | (uintptr_t)scale_out) & 15u)
+        return MXQ_E_ALIGN;
+
+    const int bias = emax_of(out_dtype) - ((flags & MXQ_FLAG_ALT_EMAX) ? 1 : 0);
+    const uint32_t dense = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
+    const int64_t threads = 64;
+    int width;
+    int64_t grid, tiles;
+    if (down) {
+        width = (O % 4 == 0) ? 4 : (O % 2 == 0) ? 2 : 1; // columns per thread
+        tiles = (O / width + threads - 1) / threads;     // per 32-row band
+        if (K / 32 > kMaxWorkgroups / tiles)
+            return MXQ_E_OVERFLOW;
+        grid = (K / 32) * tiles;
+    } else {
+        width = ((K / 32) % 2 == 0) ? 2 : 1;             // blocks per thread
+        tiles = (O + threads - 1) / threads;             // per block group
+        if (K / 32 / width > kMaxWorkgroups / tiles)
+            return MXQ_E_OVERFLOW;
+        grid = (K / 32 / width) * tiles;
+    }
+    down_kernel_fn dk = nullptr;
+    along_kernel_fn ak = nullptr;
+    if (in_dtype == MXQ_IN_BF16)
+        axis_pick<mxq::kInBF16>(out_dtype, down, width, &dk, &ak);
+    else
+        axis_pick<mxq::kInF16>(out_dtype, down, width, &dk, &ak);
+
+    const uint16_t *a0 = (const uint16_t *)in;
+    uint8_t *a1 = (uint8_t *)data_out;
+    uint8_t *a2 = (uint8_t *)scale_out;
+    int a6 = bias;
+    uint32_t a7 = dense;
+    hipError_t err;
+    if (down) {
+        uint64_t a3 = (uint64_t)O;
+        uint32_t a4 = (uint32_t)(O / width), a5 = (uint32_t)tiles;
+        void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7};
+        err = hipLaunchKernel((const void *)dk, dim3((uint32_t)grid), dim3((uint32_t)threads), args, 0,
+                              (hipStream_t)stream);
+    } else {
+        uint64_t a3 = (uint64_t)O, a4 = (uint64_t)K;
+        uint32_t a5 = (uint32_t)tiles;
+        void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7};
+        err = hipLaunchKernel((const void *)ak, dim3((uint32_t)grid), dim3((uint32_t)threads), args, 0,
+                              (hipStream_t)stream);
+    }
+    return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
+}
+
+} // extern "C"

@@ -1,0 +1,95 @@
+// mxq_dequantize_api.hip -- mxq_dequantize / mxq_dequantize_ex: validation,
+// launch geometry and dispatch to dequantize_kernel on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxq.h"
+#include "mxq_host.hpp"
+#include "mxq_dequantize_kernels.hpp"
+
+namespace {
+
+using mxq_host::check_shape;
+using mxq_host::emax_of;
+using mxq_host::kMaxF;
+using mxq_host::kMaxWorkgroups;
+
+// One 64-lane wave per workgroup, non-temporal loads and stores (the data
+// streams through once), as for the quantize.
+constexpr uint32_t kThreads = 64;
+constexpr int kNonTemporal = 3;
+
+typedef void (*dq_kernel_fn)(const uint8_t *, const uint8_t *, void *, uint64_t, uint32_t, uint32_t, uint32_t);
+
+template <int FMT, int RES> dq_kernel_fn dq_pick_nb(int nb)
+{
+    return nb == 2 ? (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 2, kNonTemporal>
+                   : (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 1, kNonTemporal>;
+}
+
+template <int RES> dq_kernel_fn dq_pick_fmt(int fmt, int nb)
+{
+    switch (fmt) {
+    case MXQ_OUT_E4M3FN: return dq_pick_nb<mxq::kOutE4M3FN, RES>(nb);
+    case MXQ_OUT_E5M2: return dq_pick_nb<mxq::kOutE5M2, RES>(nb);
+    default: return dq_pick_nb<mxq::kOutE2M1, RES>(nb);
+    }
+}
+
+// Largest normal exponent of each output format ("Block-Scale Computation",
+// The EMAX Table): the bias subtracted from a block's maximum exponent.
+
+} // namespace
+
+extern "C" {
+
+int mxq_dequantize(const void *data, const void *scale_in, int64_t P, int64_t F, int fmt, int res_dtype,
+                   void *out, void *stream)
+{
+    return mxq_dequantize_ex(data, scale_in, P, F, fmt, res_dtype, 0u, out, stream);
+}
+
+int mxq_dequantize_ex(const void *data, const void *scale_in, int64_t P, int64_t F, int fmt, int res_dtype,
+                      unsigned flags, void *out, void *stream)
+{
+    if (fmt != MXQ_OUT_E4M3FN && fmt != MXQ_OUT_E5M2 && fmt != MXQ_OUT_E2M1)
+        return MXQ_E_OUT_DTYPE;
+    if (res_dtype != MXQ_RES_F32 && res_dtype != MXQ_RES_BF16)
+        return MXQ_E_RES_DTYPE;
+    if (flags & ~(unsigned)MXQ_FLAG_DENSE_SCALE)
+        return MXQ_E_FLAGS;
+    int rc = check_shape(P, F);
+    if (rc != MXQ_OK)
+        return rc;
+    if (F > 0 && P > INT64_MAX / 4 / F)
+        return MXQ_E_OVERFLOW; // fp32 result bytes P*F*4 must fit
+    if (P == 0 || F == 0)
+        return MXQ_OK;
+    if (!data || !scale_in || !out)
+        return MXQ_E_NULL;
+    if (((uintptr_t)data | (uintptr_t)scale_in | (uintptr_t)out) & 15u)
+        return MXQ_E_ALIGN;
+
+    const int nb = (F % 8 == 0) ? 2 : 1;
+    const int64_t nstrips = F / (4 * nb);
+    const int64_t tiles_per_group = (nstrips + kThreads - 1) / kThreads;
+    const int64_t groups = P / 8;
+    if (groups > kMaxWorkgroups / tiles_per_group)
+        return MXQ_E_OVERFLOW;
+
+    dq_kernel_fn k = res_dtype == MXQ_RES_F32 ? dq_pick_fmt<mxq::kResF32>(fmt, nb)
+                                              : dq_pick_fmt<mxq::kResBF16>(fmt, nb);
+    const uint8_t *a0 = (const uint8_t *)data;
+    const uint8_t *a1 = (const uint8_t *)scale_in;
+    void *a2 = out;
+    uint64_t a3 = (uint64_t)F;
+    uint32_t a4 = (uint32_t)nstrips;
+    uint32_t a5 = (uint32_t)tiles_per_group;
+    uint32_t a6 = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
+    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6};
+    hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(groups * tiles_per_group)), dim3(kThreads),
+                                     args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
+}
+
+} // extern "C"

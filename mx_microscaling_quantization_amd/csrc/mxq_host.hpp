@@ -1,0 +1,41 @@
+// mxq_host.hpp -- host-side helpers shared by the library's entry points:
+// the EMAX table and the index-range limits of the quantize geometry.
+#pragma once
+
+#include <stdint.h>
+
+#include "mxq.h"
+
+namespace mxq_host {
+
+// The kernel indexes strips, workgroups and per-row offsets with 32-bit
+// counts and 64-bit byte offsets; these bounds keep every count in range.
+constexpr int64_t kMaxF = (int64_t)1 << 31;
+constexpr int64_t kMaxWorkgroups = ((int64_t)1 << 31) - 1;
+
+// EMAX of an output format ("MX Microscaling: Quantize, Block-Scaling and
+// E8M0", The EMAX Table).
+inline int emax_of(int out_dtype)
+{
+    switch (out_dtype) {
+    case MXQ_OUT_E4M3FN: return 8;
+    case MXQ_OUT_E5M2: return 15;
+    default: return 2;
+    }
+}
+
+// P % 8, F % 4 and the byte-count limits of a [P, F] quantize.
+inline int check_shape(int64_t P, int64_t F)
+{
+    if (P < 0 || P % 8 != 0)
+        return MXQ_E_SHAPE_P8;
+    if (F < 0 || F % 4 != 0)
+        return MXQ_E_SHAPE_F4;
+    if (F > kMaxF)
+        return MXQ_E_OVERFLOW;
+    if (F > 0 && P > INT64_MAX / 2 / F)
+        return MXQ_E_OVERFLOW; // input bytes P*F*2 must fit
+    return MXQ_OK;
+}
+
+} // namespace mxq_host

@@ -1,0 +1,101 @@
+// mxq_quantize_api.hip -- mxq_quantize / mxq_quantize_ex: validation, launch
+// geometry and dispatch on (input type, output type, strip width) to
+// quantize_kernel, launched on the caller's stream. No allocation, no state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxq.h"
+#include "mxq_host.hpp"
+#include "mxq_quantize_kernels.hpp"
+
+namespace {
+
+using mxq_host::check_shape;
+using mxq_host::emax_of;
+using mxq_host::kMaxF;
+using mxq_host::kMaxWorkgroups;
+
+// Threads per workgroup: one wave. On MI355X single-wave workgroups stream
+// this kernel's 2:1 read/write mix faster than 128- or 256-thread ones (the
+// dispatcher spreads the finer tiles more evenly over the CUs).
+constexpr uint32_t kThreads = 64;
+
+typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, uint32_t, int,
+                          uint32_t);
+
+// Row groups per thread, and non-temporal loads and stores (bit 0 | bit 1):
+// every byte is touched exactly once, so nothing is worth keeping in cache.
+constexpr int kGroupsPerThread = 1;
+constexpr int kNonTemporal = 3;
+
+template <int IN, int OUT> kernel_fn pick_nb(int nb)
+{
+    return nb == 2 ? (kernel_fn)mxq::quantize_kernel<IN, OUT, 2, kGroupsPerThread, kNonTemporal>
+                   : (kernel_fn)mxq::quantize_kernel<IN, OUT, 1, kGroupsPerThread, kNonTemporal>;
+}
+
+template <int IN> kernel_fn pick_out(int out_dtype, int nb)
+{
+    switch (out_dtype) {
+    case MXQ_OUT_E4M3FN: return pick_nb<IN, mxq::kOutE4M3FN>(nb);
+    case MXQ_OUT_E5M2: return pick_nb<IN, mxq::kOutE5M2>(nb);
+    default: return pick_nb<IN, mxq::kOutE2M1>(nb);
+    }
+}
+
+} // namespace
+
+extern "C" {
+
+int mxq_quantize(const void *in, int64_t P, int64_t F, int in_dtype, int out_dtype, void *data_out,
+                 void *scale_out, void *stream)
+{
+    return mxq_quantize_ex(in, P, F, in_dtype, out_dtype, 0u, data_out, scale_out, stream);
+}
+
+int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_dtype, unsigned flags,
+                    void *data_out, void *scale_out, void *stream)
+{
+    if (in_dtype != MXQ_IN_BF16 && in_dtype != MXQ_IN_F16)
+        return MXQ_E_IN_DTYPE;
+    if (out_dtype != MXQ_OUT_E4M3FN && out_dtype != MXQ_OUT_E5M2 && out_dtype != MXQ_OUT_E2M1)
+        return MXQ_E_OUT_DTYPE;
+    if (flags & ~(unsigned)(MXQ_FLAG_ALT_EMAX | MXQ_FLAG_DENSE_SCALE))
+        return MXQ_E_FLAGS;
+    int rc = check_shape(P, F);
+    if (rc != MXQ_OK)
+        return rc;
+    if (P == 0 || F == 0)
+        return MXQ_OK;
+    if (!in || !data_out || !scale_out)
+        return MXQ_E_NULL;
+    if (((uintptr_t)in | (uintptr_t)data_out | (uintptr_t)scale_out) & 15u)
+        return MXQ_E_ALIGN;
+
+    const int nb = (F % 8 == 0) ? 2 : 1;
+    const int64_t nstrips = F / (4 * nb);
+    const uint32_t threads = kThreads;
+    const int64_t tiles_per_band = (nstrips + threads - 1) / threads;
+    const int64_t groups = P / 8;
+    const int64_t bands = (groups + kGroupsPerThread - 1) / kGroupsPerThread;
+    if (bands > kMaxWorkgroups / tiles_per_band)
+        return MXQ_E_OVERFLOW;
+
+    kernel_fn k = in_dtype == MXQ_IN_BF16 ? pick_out<mxq::kInBF16>(out_dtype, nb)
+                                          : pick_out<mxq::kInF16>(out_dtype, nb);
+    const uint16_t *a0 = (const uint16_t *)in;
+    uint8_t *a1 = (uint8_t *)data_out;
+    uint8_t *a2 = (uint8_t *)scale_out;
+    uint64_t a3 = (uint64_t)F;
+    uint32_t a4 = (uint32_t)nstrips;
+    uint32_t a5 = (uint32_t)tiles_per_band;
+    uint32_t a6 = (uint32_t)groups;
+    int a7 = emax_of(out_dtype) - ((flags & MXQ_FLAG_ALT_EMAX) ? 1 : 0);
+    uint32_t a8 = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
+    void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7, &a8};
+    hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(bands * tiles_per_band)), dim3(threads),
+                                     args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
+}
+
+} // extern "C"

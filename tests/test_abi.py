@@ -37,7 +37,8 @@ def _header_enums():
 def test_library_exports_every_declared_function():
     lib = mxq.load()
     names = _declared_functions()
-    assert {"mxq_quantize", "mxq_quantize_ex", "mxq_dequantize", "mxq_dequantize_ex", "mxq_scaled_matmul",
+    assert {"mxq_quantize", "mxq_quantize_ex", "mxq_quantize_axis", "mxq_dequantize", "mxq_dequantize_ex",
+            "mxq_scaled_matmul", "mxq_scaled_matmul_quantize",
             "mxq_data_bytes",
             "mxq_scale_image_bytes", "mxq_scale_bytes", "mxq_result_bytes", "mxq_status_string",
             "mxq_abi_version"} <= set(names)
@@ -213,6 +214,31 @@ def test_scaled_matmul_quantize_validation_errors_before_launch():
     assert mq(32, 8, 4, ptrs=(g, g, g, g, g + 8, g)) == e["MXQ_E_ALIGN"]
     for flags in (0, 1, 2, 3):                                   # every documented flag combination passes validation
         assert mq(32, 8, 4, flags=flags, ptrs=(None,) * 6) == e["MXQ_E_NULL"]
+
+
+def test_quantize_axis_validation_errors_before_launch():
+    e = _header_enums()
+    lib = mxq.load()
+    g = 4096
+
+    def qa(R, C, dim=-1, ind=0, out=0, flags=0, ptrs=(g, g, g)):
+        i, d, s = ptrs
+        return lib.mxq_quantize_axis(i, R, C, ind, out, dim, flags, d, s, None)
+
+    assert qa(8, 32, ind=2) == e["MXQ_E_IN_DTYPE"]
+    assert qa(8, 32, out=3) == e["MXQ_E_OUT_DTYPE"]
+    assert qa(8, 32, flags=4) == e["MXQ_E_FLAGS"]
+    for bad in (2, -3, 5):
+        assert qa(32, 32, dim=bad) == e["MXQ_E_DIM"]
+    assert qa(8, 36, dim=-1) == e["MXQ_E_SHAPE_P8"]                # blocks along rows need C % 32
+    assert qa(36, 8, dim=-2) == e["MXQ_E_SHAPE_P8"]                # blocks down columns need R % 32
+    assert qa(36, 8, dim=0) == e["MXQ_E_SHAPE_P8"]                 # 0 is -2 folded by the rank
+    assert qa(1 << 31, 32, dim=-1) == e["MXQ_E_OVERFLOW"]
+    assert qa(0, 32, ptrs=(None,) * 3) == 0 and qa(32, 0, dim=-2, ptrs=(None,) * 3) == 0
+    assert qa(8, 32, ptrs=(g, None, g)) == e["MXQ_E_NULL"]
+    assert qa(8, 32, ptrs=(g + 2, g, g)) == e["MXQ_E_ALIGN"]
+    assert mxq.axis_view_shape(12, 64, -1) == (16, 48) and mxq.axis_view_shape(64, 12, -2) == (16, 48)
+    assert lib.mxq_status_string(e["MXQ_E_DIM"]).decode().startswith("quantize axis")
 
 
 def test_empty_tensors_are_noops():
