@@ -27,26 +27,22 @@ template <int IN, int OUT> down_kernel_fn down_pick_nb(int nb)
     }
 }
 
-template <int IN, int OUT> along_kernel_fn along_pick_gb(int gb)
-{
-    return gb == 2 ? (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT, 2>
-                   : (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT, 1>;
-}
+template <int IN, int OUT> along_kernel_fn along_pick(int) { return (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT>; }
 
 template <int IN> void axis_pick(int out_dtype, int down, int width, down_kernel_fn *d, along_kernel_fn *a)
 {
     switch (out_dtype) {
     case MXQ_OUT_E4M3FN:
         *d = down ? down_pick_nb<IN, mxq::kOutE4M3FN>(width) : nullptr;
-        *a = down ? nullptr : along_pick_gb<IN, mxq::kOutE4M3FN>(width);
+        *a = down ? nullptr : along_pick<IN, mxq::kOutE4M3FN>(width);
         break;
     case MXQ_OUT_E5M2:
         *d = down ? down_pick_nb<IN, mxq::kOutE5M2>(width) : nullptr;
-        *a = down ? nullptr : along_pick_gb<IN, mxq::kOutE5M2>(width);
+        *a = down ? nullptr : along_pick<IN, mxq::kOutE5M2>(width);
         break;
     default:
         *d = down ? down_pick_nb<IN, mxq::kOutE2M1>(width) : nullptr;
-        *a = down ? nullptr : along_pick_gb<IN, mxq::kOutE2M1>(width);
+        *a = down ? nullptr : along_pick<IN, mxq::kOutE2M1>(width);
         break;
     }
 }
@@ -98,11 +94,12 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
             return MXQ_E_OVERFLOW;
         grid = (K / 32) * tiles;
     } else {
-        width = ((K / 32) % 2 == 0) ? 2 : 1;             // blocks per thread
-        tiles = (O + threads - 1) / threads;             // per block group
-        if (K / 32 / width > kMaxWorkgroups / tiles)
+        width = 0;
+        tiles = (O + mxq::kAlongRows - 1) / mxq::kAlongRows;             // 64-row tiles
+        const int64_t ktiles = (K + mxq::kAlongTileK - 1) / mxq::kAlongTileK; // 256-element tiles
+        if (ktiles > kMaxWorkgroups / tiles)
             return MXQ_E_OVERFLOW;
-        grid = (K / 32 / width) * tiles;
+        grid = ktiles * tiles;
     }
     down_kernel_fn dk = nullptr;
     along_kernel_fn ak = nullptr;
@@ -127,8 +124,7 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
         uint64_t a3 = (uint64_t)O, a4 = (uint64_t)K;
         uint32_t a5 = (uint32_t)tiles;
         void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7};
-        err = hipLaunchKernel((const void *)ak, dim3((uint32_t)grid), dim3((uint32_t)threads), args, 0,
-                              (hipStream_t)stream);
+        err = hipLaunchKernel((const void *)ak, dim3((uint32_t)grid), dim3(256), args, 0, (hipStream_t)stream);
     }
     return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
 }

@@ -131,57 +131,82 @@ __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__res
 
 // Blocks along the rows (dim -1) of X [M][K] (row pitch K).
 //
-// A thread owns row m and GB consecutive blocks g0 .. g0 + GB - 1 along it:
-// 64*GB contiguous bytes, loaded as 16-byte pieces. Block g's view rows are
-// p = 8g + pr, and row m's container in view row p is elements 4p .. 4p + 3
-// of its block, i.e. dwords 2pr, 2pr + 1 of the block's 16. The container
-// goes to p * 4M + 4m (FP8) / p * 2M + 2m (FP4): a wave of consecutive rows
-// writes 256 (128) contiguous bytes per view row. The E8M0 byte goes to the
-// placed (or dense) scale row of g at column m.
-//   tiles_m   ceil(M / 64); the grid is tiles_m x (K / 32 / GB)
-template <int IN, int OUT, int GB>
-__global__ __launch_bounds__(64) void quantize_along_kernel(const uint16_t *__restrict__ in,
-                                                            uint8_t *__restrict__ data,
-                                                            uint8_t *__restrict__ scale, uint64_t M,
-                                                            uint64_t K, uint32_t tiles_m, int emax_bias,
-                                                            uint32_t dense)
+// A block is 32 contiguous elements of one row, but its codes go to 8 view
+// rows at column m, so a wave must cover 64 consecutive rows to store
+// contiguously -- and 64 rows read one block each would touch 64 cache lines
+// per load. So a 256-thread workgroup stages a tile of 64 rows x 256
+// elements (8 blocks) in LDS with coalesced loads (a wave's load is two
+// 512-byte row segments), then thread (row r = t mod 64, blocks 2w and
+// 2w + 1 for wave w) quantizes from LDS. The LDS row pitch is 528 bytes: the
+// 16-byte skew per row puts the 16 rows that 16 lanes read in distinct
+// banks. Block g's view rows are p = 8g + pr, and row m's container in view
+// row p is elements 4p .. 4p + 3 of the block, i.e. dwords 2pr, 2pr + 1 of
+// its 16; it goes to p * 4M + 4m (FP8) / p * 2M + 2m (FP4), so a wave
+// writes 256 (128) contiguous bytes per view row. The E8M0 byte goes to
+// the placed (or dense) scale row of g at column m.
+//   tiles_m   ceil(M / 64); the grid is tiles_m x ceil(K / 256)
+constexpr uint32_t kAlongRows = 64;
+constexpr uint32_t kAlongTileK = 256;
+constexpr uint32_t kAlongPitch = 2 * kAlongTileK + 16;
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(256) void quantize_along_kernel(const uint16_t *__restrict__ in,
+                                                             uint8_t *__restrict__ data,
+                                                             uint8_t *__restrict__ scale, uint64_t M,
+                                                             uint64_t K, uint32_t tiles_m, int emax_bias,
+                                                             uint32_t dense)
 {
-    static_assert(GB == 1 || GB == 2, "1 or 2 blocks per thread");
-    const uint32_t bg = blockIdx.x / tiles_m;
-    const uint64_t m = (uint64_t)(blockIdx.x - bg * tiles_m) * 64u + threadIdx.x;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kAlongRows * kAlongPitch];
+    const uint32_t tk = blockIdx.x / tiles_m;
+    const uint64_t m0 = (uint64_t)(blockIdx.x - tk * tiles_m) * kAlongRows;
+    const uint64_t k0 = (uint64_t)tk * kAlongTileK;
+    const uint32_t nblk = (uint32_t)min((uint64_t)(kAlongTileK / 32), (K - k0) / 32);
+    const uint32_t t = threadIdx.x;
+
+    // 64 rows x 32 pieces of 16 bytes; piece q: row q / 32, piece q mod 32
+#pragma unroll
+    for (uint32_t i = 0; i < 8; i++) {
+        const uint32_t q = t + 256u * i;
+        const uint32_t r = q >> 5, c = q & 31u;
+        if (m0 + r < M && c < 4u * nblk) {
+            const u32x4_t v = load<1>(reinterpret_cast<const u32x4_t *>(in + (m0 + r) * K + k0 + 8u * c));
+            *reinterpret_cast<u32x4_t *>(tile + r * kAlongPitch + 16u * c) = v;
+        }
+    }
+    __syncthreads();
+
+    const uint32_t r = t & (kAlongRows - 1);
+    const uint64_t m = m0 + r;
     if (m >= M)
         return;
-    const uint32_t g0 = bg * GB;
-
-    uint32_t d[GB][16];
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(in + m * K + 32ull * g0);
-#pragma unroll
-    for (int b = 0; b < GB; b++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const u32x4_t t = load<1>(src + 4 * b + q);
-            d[b][4 * q + 0] = t.x;
-            d[b][4 * q + 1] = t.y;
-            d[b][4 * q + 2] = t.z;
-            d[b][4 * q + 3] = t.w;
-        }
-
     const uint64_t F = 4 * M;
 #pragma unroll
-    for (int b = 0; b < GB; b++) {
+    for (uint32_t bb = 0; bb < 2; bb++) {
+        const uint32_t b = 2u * (t >> 6) + bb;
+        if (b >= nblk)
+            break;
+        uint32_t d[16];
+#pragma unroll
+        for (uint32_t q = 0; q < 4; q++) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(tile + r * kAlongPitch + 64u * b + 16u * q);
+            d[4 * q + 0] = v.x;
+            d[4 * q + 1] = v.y;
+            d[4 * q + 2] = v.z;
+            d[4 * q + 3] = v.w;
+        }
         uint32_t mm = 0;
 #pragma unroll
         for (int k = 0; k < 16; k++)
-            mm = pk_max_u16(mm, d[b][k] & 0x7FFF7FFFu);
+            mm = pk_max_u16(mm, d[k] & 0x7FFF7FFFu);
         const uint32_t mag = max(mm & 0xFFFFu, mm >> 16);
         uint32_t e[1] = {block_e8m0<IN>(mag, emax_bias)};
         const float s = e8m0_to_scale(e[0]);
         const bool special = mag > InfBits<IN>::value || e[0] == 254u;
-        const uint64_t g = g0 + b;
+        const uint64_t g = k0 / 32 + b;
 #pragma unroll
         for (int pr = 0; pr < 8; pr++) {
             const uint64_t p = g * 8u + pr;
-            uint32_t w[2] = {d[b][2 * pr], d[b][2 * pr + 1]};
+            uint32_t w[2] = {d[2 * pr], d[2 * pr + 1]};
             uint32_t out[1];
             if constexpr (OUT == kOutE2M1)
                 out[0] = fp4_container<IN, 0>(0u, w[0], w[1], s);
