@@ -27,7 +27,11 @@ template <int IN, int OUT> down_kernel_fn down_pick_nb(int nb)
     }
 }
 
-template <int IN, int OUT> along_kernel_fn along_pick(int) { return (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT>; }
+template <int IN, int OUT> along_kernel_fn along_pick(int narrow)
+{
+    return narrow ? (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT, 1>
+                  : (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT, 0>;
+}
 
 template <int IN> void axis_pick(int out_dtype, int down, int width, down_kernel_fn *d, along_kernel_fn *a)
 {
@@ -94,9 +98,9 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
             return MXQ_E_OVERFLOW;
         grid = (K / 32) * tiles;
     } else {
-        width = 0;
-        tiles = (O + mxq::kAlongRows - 1) / mxq::kAlongRows;             // 64-row tiles
-        const int64_t ktiles = (K + mxq::kAlongTileK - 1) / mxq::kAlongTileK; // 256-element tiles
+        width = O % 4 != 0;                                   // rows of the view not 16-byte aligned
+        tiles = (O + mxq::kAlongRows - 1) / mxq::kAlongRows; // row tiles
+        const int64_t ktiles = (K / 32 + 1) / 2;              // two blocks per tile
         if (ktiles > kMaxWorkgroups / tiles)
             return MXQ_E_OVERFLOW;
         grid = ktiles * tiles;
@@ -124,7 +128,8 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
         uint64_t a3 = (uint64_t)O, a4 = (uint64_t)K;
         uint32_t a5 = (uint32_t)tiles;
         void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7};
-        err = hipLaunchKernel((const void *)ak, dim3((uint32_t)grid), dim3(256), args, 0, (hipStream_t)stream);
+        err = hipLaunchKernel((const void *)ak, dim3((uint32_t)grid), dim3(64 * mxq::kAlongWaves), args, 0,
+                              (hipStream_t)stream);
     }
     return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
 }

@@ -13,7 +13,8 @@
 // Both kernels do the plain quantize's arithmetic with its own helpers
 // (packed 16-bit block max, E8M0 clamp, scaled conversions, saturation,
 // special-code pass); they differ only in how the 32 elements of a block
-// reach a thread and where its codes go. One HBM pass, non-temporal hints.
+// reach the lanes that quantize them and where its codes go. One HBM pass,
+// non-temporal hints.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -129,98 +130,159 @@ __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__res
     store_bytes<NB, 1>(scale + slot * N + n0, packed);
 }
 
+// Max of x over the four lanes of each lane quad (DPP quad permutations; every
+// lane of the wave must be active).
+__device__ __forceinline__ uint32_t quad_max(uint32_t x)
+{
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false)); // lane ^ 1
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false)); // lane ^ 2
+    return x;
+}
+
 // Blocks along the rows (dim -1) of X [M][K] (row pitch K).
 //
-// A block is 32 contiguous elements of one row, but its codes go to 8 view
-// rows at column m, so a wave must cover 64 consecutive rows to store
-// contiguously -- and 64 rows read one block each would touch 64 cache lines
-// per load. So a 256-thread workgroup stages a tile of 64 rows x 256
-// elements (8 blocks) in LDS with coalesced loads (a wave's load is two
-// 512-byte row segments), then thread (row r = t mod 64, blocks 2w and
-// 2w + 1 for wave w) quantizes from LDS. The LDS row pitch is 528 bytes: the
-// 16-byte skew per row puts the 16 rows that 16 lanes read in distinct
-// banks. Block g's view rows are p = 8g + pr, and row m's container in view
-// row p is elements 4p .. 4p + 3 of the block, i.e. dwords 2pr, 2pr + 1 of
-// its 16; it goes to p * 4M + 4m (FP8) / p * 2M + 2m (FP4), so a wave
-// writes 256 (128) contiguous bytes per view row. The E8M0 byte goes to
-// the placed (or dense) scale row of g at column m.
-//   tiles_m   ceil(M / 64); the grid is tiles_m x ceil(K / 256)
-constexpr uint32_t kAlongRows = 64;
-constexpr uint32_t kAlongTileK = 256;
-constexpr uint32_t kAlongPitch = 2 * kAlongTileK + 16;
+// A block is 32 contiguous elements of one row, and its codes go to 8 view
+// rows at column m: 4 bytes (FP8) or 2 bytes (FP4) per view row. A lane per
+// block would read one cache line per lane and write 4-byte pieces, so the
+// codes go through LDS. A workgroup of kAlongWaves waves owns kAlongRows
+// consecutive rows x 2 blocks (128 bytes of each row); wave w owns rows
+// 128w .. 128w + 127 of the tile.
+//  * Load: lane l reads 16-byte chunk c = l mod 8 (quarter q = c mod 4 of
+//    block c/4: elements 8q .. 8q + 7, the containers of view rows 2q and
+//    2q + 1) of wave row 4i + (k mod 4) + 32*(k/4), i = l/8, for its loads
+//    k = 0..15. One load instruction reads 8 rows x 128 contiguous bytes.
+//  * Block max: a lane-local packed max of its 8 elements, then two DPP steps
+//    across the lane quad that holds the block's four quarters.
+//  * Codes: after each four loads a lane holds four consecutive rows' codes
+//    for each of its two view rows (16 or 8 bytes) and writes them into
+//    that view row's LDS strip of kAlongRows codes; the quad's first lane
+//    writes the four E8M0 bytes into the block's strip.
+//  * Store: after one barrier each of the tile's 16 view rows leaves as one
+//    contiguous run of kAlongRows codes (1 KiB for FP8), 16 (FP8) or 8 (FP4)
+//    bytes per lane, and each scale strip as 4 bytes per lane. With NARROW
+//    (M % 4 != 0: view rows are not 16-byte aligned) every lane stores one
+//    row: 4 or 2 code bytes and 1 scale byte.
+// Row tiles vary fastest over the grid (ceil(M / kAlongRows) x ceil(K / 64)),
+// so the workgroups in flight write few view rows, each in long runs.
+constexpr uint32_t kAlongWaves = 2;
+constexpr uint32_t kAlongWaveRows = 128;
+constexpr uint32_t kAlongRows = kAlongWaves * kAlongWaveRows;
 
-template <int IN, int OUT>
-__global__ __launch_bounds__(256) void quantize_along_kernel(const uint16_t *__restrict__ in,
-                                                             uint8_t *__restrict__ data,
-                                                             uint8_t *__restrict__ scale, uint64_t M,
-                                                             uint64_t K, uint32_t tiles_m, int emax_bias,
-                                                             uint32_t dense)
+template <int IN, int OUT, int NARROW>
+__global__ __launch_bounds__(64 * kAlongWaves) void quantize_along_kernel(const uint16_t *__restrict__ in,
+                                                                          uint8_t *__restrict__ data,
+                                                                          uint8_t *__restrict__ scale, uint64_t M,
+                                                                          uint64_t K, uint32_t tiles_m, int emax_bias,
+                                                                          uint32_t dense)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kAlongRows * kAlongPitch];
-    const uint32_t tk = blockIdx.x / tiles_m;
-    const uint64_t m0 = (uint64_t)(blockIdx.x - tk * tiles_m) * kAlongRows;
-    const uint64_t k0 = (uint64_t)tk * kAlongTileK;
-    const uint32_t nblk = (uint32_t)min((uint64_t)(kAlongTileK / 32), (K - k0) / 32);
-    const uint32_t t = threadIdx.x;
+    constexpr uint32_t RT = kAlongRows, KG = kAlongWaveRows / 32; // four-load groups per lane
+    constexpr uint32_t CB = OUT == kOutE2M1 ? 2 : 4;              // code bytes per row and view row
+    constexpr uint32_t PITCH = RT * CB + 16;                      // LDS bytes per view-row strip
+    static_assert(RT % 256 == 0 && 16 % kAlongWaves == 0, "whole 4-row lanes per store, whole view rows per wave");
+    __shared__ __attribute__((aligned(16))) uint8_t codes[16 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t e8m0[2 * RT];
 
-    // 64 rows x 32 pieces of 16 bytes; piece q: row q / 32, piece q mod 32
+    const uint32_t t = threadIdx.x, w = t >> 6, l = t & 63u;
+    const uint32_t c = l & 7u, i = l >> 3, q = c & 3u, bl = c >> 2;
+    const uint32_t tk = blockIdx.x / tiles_m;
+    const uint64_t m0 = (uint64_t)(blockIdx.x - tk * tiles_m) * RT;
+    const uint64_t G = K / 32;
+    const uint64_t g = (uint64_t)tk * 2u + bl;
+
+    u32x4_t v[4 * KG];
 #pragma unroll
-    for (uint32_t i = 0; i < 8; i++) {
-        const uint32_t q = t + 256u * i;
-        const uint32_t r = q >> 5, c = q & 31u;
-        if (m0 + r < M && c < 4u * nblk) {
-            const u32x4_t v = load<1>(reinterpret_cast<const u32x4_t *>(in + (m0 + r) * K + k0 + 8u * c));
-            *reinterpret_cast<u32x4_t *>(tile + r * kAlongPitch + 16u * c) = v;
+    for (uint32_t k = 0; k < 4 * KG; k++) {
+        const uint64_t m = m0 + kAlongWaveRows * w + 4u * i + (k & 3u) + 32u * (k >> 2);
+        v[k] = u32x4_t{0u, 0u, 0u, 0u};
+        if (g < G && m < M)
+            v[k] = load<1>(reinterpret_cast<const u32x4_t *>(in + m * K + g * 32u + 8u * q));
+    }
+
+#pragma unroll
+    for (uint32_t kg = 0; kg < KG; kg++) {
+        uint32_t lo[4], hi[4], eb[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const u32x4_t x = v[4 * kg + j];
+            uint32_t mm = pk_max_u16(x.x & 0x7FFF7FFFu, x.y & 0x7FFF7FFFu);
+            mm = pk_max_u16(mm, x.z & 0x7FFF7FFFu);
+            mm = pk_max_u16(mm, x.w & 0x7FFF7FFFu);
+            const uint32_t mag = quad_max(max(mm & 0xFFFFu, mm >> 16));
+            uint32_t e[1] = {block_e8m0<IN>(mag, emax_bias)};
+            const float s = e8m0_to_scale(e[0]);
+            uint32_t w0[2] = {x.x, x.y}, w1[2] = {x.z, x.w};
+            uint32_t o0[1], o1[1];
+            if constexpr (OUT == kOutE2M1) {
+                o0[0] = fp4_container<IN, 0>(0u, w0[0], w0[1], s);
+                o1[0] = fp4_container<IN, 0>(0u, w1[0], w1[1], s);
+            } else {
+                o0[0] = fp8x4<IN, OUT>(w0[0], w0[1], s);
+                o1[0] = fp8x4<IN, OUT>(w1[0], w1[1], s);
+            }
+            if (mag > InfBits<IN>::value || e[0] == 254u) {
+                fix_special_codes<IN, OUT, 1>(w0, e, o0);
+                fix_special_codes<IN, OUT, 1>(w1, e, o1);
+            }
+            lo[j] = o0[0];
+            hi[j] = o1[0];
+            eb[j] = e[0];
         }
+        const uint32_t r = kAlongWaveRows * w + 4u * i + 32u * kg; // first of the lane's four tile rows
+        uint8_t *s0 = codes + (8u * bl + 2u * q) * PITCH + CB * r;
+        if constexpr (OUT == kOutE2M1) {
+            *reinterpret_cast<u32x2_t *>(s0) = u32x2_t{lo[0] | lo[1] << 16, lo[2] | lo[3] << 16};
+            *reinterpret_cast<u32x2_t *>(s0 + PITCH) = u32x2_t{hi[0] | hi[1] << 16, hi[2] | hi[3] << 16};
+        } else {
+            *reinterpret_cast<u32x4_t *>(s0) = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+            *reinterpret_cast<u32x4_t *>(s0 + PITCH) = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+        }
+        if (q == 0)
+            *reinterpret_cast<uint32_t *>(e8m0 + bl * RT + r) = eb[0] | eb[1] << 8 | eb[2] << 16 | eb[3] << 24;
     }
     __syncthreads();
 
-    const uint32_t r = t & (kAlongRows - 1);
-    const uint64_t m = m0 + r;
-    if (m >= M)
-        return;
     const uint64_t F = 4 * M;
+    constexpr uint32_t RPL = NARROW ? 1 : 4;     // rows per lane and store
+    constexpr uint32_t VPW = 16 / kAlongWaves;   // view rows per wave
 #pragma unroll
-    for (uint32_t bb = 0; bb < 2; bb++) {
-        const uint32_t b = 2u * (t >> 6) + bb;
-        if (b >= nblk)
-            break;
-        uint32_t d[16];
+    for (uint32_t j = 0; j < VPW; j++) {
+        const uint32_t vr = VPW * w + j;
+        const uint64_t gg = (uint64_t)tk * 2u + (vr >> 3);
+        const uint64_t p = gg * 8u + (vr & 7u);
 #pragma unroll
-        for (uint32_t q = 0; q < 4; q++) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(tile + r * kAlongPitch + 64u * b + 16u * q);
-            d[4 * q + 0] = v.x;
-            d[4 * q + 1] = v.y;
-            d[4 * q + 2] = v.z;
-            d[4 * q + 3] = v.w;
+        for (uint32_t s = 0; s < RT / (64 * RPL); s++) {
+            const uint32_t r = 64u * RPL * s + RPL * l;
+            if (gg < G && m0 + r < M) {
+                const uint8_t *src = codes + vr * PITCH + CB * r;
+                uint8_t *dst = OUT == kOutE2M1 ? data + (p * F) / 2 + 2u * (m0 + r) : data + p * F + 4u * (m0 + r);
+                if constexpr (NARROW) {
+                    if constexpr (OUT == kOutE2M1)
+                        store<1>(reinterpret_cast<uint16_t *>(dst), *reinterpret_cast<const uint16_t *>(src));
+                    else
+                        store<1>(reinterpret_cast<uint32_t *>(dst), *reinterpret_cast<const uint32_t *>(src));
+                } else {
+                    if constexpr (OUT == kOutE2M1)
+                        store<1>(reinterpret_cast<u32x2_t *>(dst), *reinterpret_cast<const u32x2_t *>(src));
+                    else
+                        store<1>(reinterpret_cast<u32x4_t *>(dst), *reinterpret_cast<const u32x4_t *>(src));
+                }
+            }
         }
-        uint32_t mm = 0;
+    }
+    // the two scale strips: the E8M0 of block gg for rows m0 .. m0 + RT - 1
+    // goes to the placed (or dense) row of gg at column m
 #pragma unroll
-        for (int k = 0; k < 16; k++)
-            mm = pk_max_u16(mm, d[k] & 0x7FFF7FFFu);
-        const uint32_t mag = max(mm & 0xFFFFu, mm >> 16);
-        uint32_t e[1] = {block_e8m0<IN>(mag, emax_bias)};
-        const float s = e8m0_to_scale(e[0]);
-        const bool special = mag > InfBits<IN>::value || e[0] == 254u;
-        const uint64_t g = k0 / 32 + b;
-#pragma unroll
-        for (int pr = 0; pr < 8; pr++) {
-            const uint64_t p = g * 8u + pr;
-            uint32_t w[2] = {d[2 * pr], d[2 * pr + 1]};
-            uint32_t out[1];
-            if constexpr (OUT == kOutE2M1)
-                out[0] = fp4_container<IN, 0>(0u, w[0], w[1], s);
+    for (uint32_t idx = t; idx < 2 * RT / RPL; idx += 64 * kAlongWaves) {
+        const uint32_t strip = idx / (RT / RPL), r = RPL * (idx - strip * (RT / RPL));
+        const uint64_t gg = (uint64_t)tk * 2u + strip;
+        if (gg < G && m0 + r < M) {
+            const uint64_t slot = dense ? gg : (gg & 3u) + 32u * (gg >> 2);
+            if constexpr (NARROW)
+                store<1>(scale + slot * M + m0 + r, e8m0[strip * RT + r]);
             else
-                out[0] = fp8x4<IN, OUT>(w[0], w[1], s);
-            if (special)
-                fix_special_codes<IN, OUT, 1>(w, e, out);
-            if constexpr (OUT == kOutE2M1)
-                store_bytes<2, 1>(data + (p * F) / 2 + 2 * m, out);
-            else
-                store_bytes<4, 1>(data + p * F + 4 * m, out);
+                store<1>(reinterpret_cast<uint32_t *>(scale + slot * M + m0 + r),
+                         *reinterpret_cast<const uint32_t *>(e8m0 + strip * RT + r));
         }
-        const uint64_t slot = dense ? g : (g & 3u) + 32u * (g >> 2);
-        store_bytes<1, 1>(scale + slot * M + m, e);
     }
 }
 

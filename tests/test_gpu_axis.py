@@ -55,8 +55,12 @@ def run(bits, in_dtype, fmt, dim, alt=False, dense=False):
     return x
 
 
+# dim -1 rows (R) cover both store widths (R % 4 == 0: 16/8-byte stores; else
+# one row per lane), partial 256-row tiles and odd block counts (C/32 odd:
+# the last tile holds one block)
 SHAPES = [(-2, 32, 4), (-2, 64, 36), (-2, 96, 64), (-2, 128, 130), (-2, 256, 257), (-2, 1024, 1000),
-          (-1, 13, 96), (-1, 64, 64), (-1, 100, 256), (-1, 1000, 512), (-1, 7, 32), (1, 70, 160), (0, 160, 70)]
+          (-1, 13, 96), (-1, 64, 64), (-1, 100, 256), (-1, 1000, 512), (-1, 7, 32), (1, 70, 160), (0, 160, 70),
+          (-1, 4, 32), (-1, 260, 96), (-1, 516, 1056), (-1, 1001, 160), (-1, 256, 64)]
 
 
 @pytest.mark.parametrize("in_dtype,fmt", [("bf16", "e4m3fn"), ("bf16", "e5m2"), ("bf16", "e2m1"),
