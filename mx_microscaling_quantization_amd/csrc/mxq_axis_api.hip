@@ -122,7 +122,11 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
         uint64_t a3 = (uint64_t)O;
         uint32_t a4 = (uint32_t)(O / width), a5 = (uint32_t)tiles;
         void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7};
-        err = hipLaunchKernel((const void *)dk, dim3((uint32_t)grid), dim3((uint32_t)threads), args, 0,
+        // at most 8 waves per CU once the tensor outgrows the cache (1.07 G
+        // elements: 514 us uncapped, 487 us capped); the along kernel's own
+        // LDS tile already sets its residency, and more reserve slows it
+        const uint32_t lds = mxq_host::occupancy_cap_lds(K * O, 3, (uint32_t)threads, 8);
+        err = hipLaunchKernel((const void *)dk, dim3((uint32_t)grid), dim3((uint32_t)threads), args, lds,
                               (hipStream_t)stream);
     } else {
         uint64_t a3 = (uint64_t)O, a4 = (uint64_t)K;

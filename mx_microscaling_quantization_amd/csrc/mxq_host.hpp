@@ -1,5 +1,6 @@
 // mxq_host.hpp -- host-side helpers shared by the library's entry points:
-// the EMAX table and the index-range limits of the quantize geometry.
+// the EMAX table, the index-range limits of the quantize geometry and the
+// occupancy cap of the streaming kernels.
 #pragma once
 
 #include <stdint.h>
@@ -22,6 +23,24 @@ inline int emax_of(int out_dtype)
     case MXQ_OUT_E5M2: return 15;
     default: return 2;
     }
+}
+
+// LDS to reserve per workgroup of `wg_threads` threads so that a CU holds at
+// most `waves_per_cu` waves of a streaming kernel, or 0 (no cap). The
+// kernels never touch the reserve; it only limits residency. Once a call's
+// traffic (elements x about `bytes_per_element`) exceeds the 256 MiB
+// Infinity Cache, the stream runs from HBM, and there fewer waves in flight
+// measured faster (the workgroups in flight keep fewer DRAM pages open);
+// within the cache full occupancy is faster, so nothing is reserved.
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;
+constexpr uint32_t kLdsBytesPerCU = 160u * 1024u;
+inline uint32_t occupancy_cap_lds(int64_t elements, int64_t bytes_per_element, uint32_t wg_threads,
+                                  uint32_t waves_per_cu)
+{
+    const uint32_t wgs = waves_per_cu / (wg_threads / 64);
+    if (wgs == 0 || elements <= kInfinityCacheBytes / bytes_per_element)
+        return 0;
+    return kLdsBytesPerCU / wgs;
 }
 
 // P % 8, F % 4 and the byte-count limits of a [P, F] quantize.

@@ -15,10 +15,26 @@ using mxq_host::emax_of;
 using mxq_host::kMaxF;
 using mxq_host::kMaxWorkgroups;
 
-// Threads per workgroup: one wave. On MI355X single-wave workgroups stream
-// this kernel's 2:1 read/write mix faster than 128- or 256-thread ones (the
-// dispatcher spreads the finer tiles more evenly over the CUs).
-constexpr uint32_t kThreads = 64;
+// Workgroup width and residency. When the data rows start on 128-byte
+// lines (row pitch F bytes for FP8, F/2 for FP4, a multiple of 128),
+// single-wave workgroups stream this kernel's 2:1 read/write mix fastest,
+// with at most 10 waves per CU once the tensor outgrows the cache (measured
+// on the 1.07 G-element bf16 -> e4m3fn input: 488 us uncapped, 473 us
+// capped). When they do not, every workgroup's first and last line of each
+// row is shared with its neighbour, and wider workgroups make those shared
+// lines rarer: 128 threads and 10 waves per CU for 2-block strips, 256
+// threads uncapped for 1-block strips (F = 8200: 729 -> 572 us; F = 8188:
+// 944 -> 609 us).
+struct LaunchShape {
+    uint32_t threads, waves_per_cu;
+};
+inline LaunchShape launch_shape(int64_t F, int out_dtype, int nb)
+{
+    const int64_t pitch = out_dtype == MXQ_OUT_E2M1 ? F / 2 : F;
+    if (pitch % 128 == 0)
+        return {64, 10};
+    return nb == 2 ? LaunchShape{128, 10} : LaunchShape{256, 0};
+}
 
 typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, uint32_t, int,
                           uint32_t);
@@ -74,7 +90,9 @@ int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_
 
     const int nb = (F % 8 == 0) ? 2 : 1;
     const int64_t nstrips = F / (4 * nb);
-    const uint32_t threads = kThreads;
+    const LaunchShape shape = launch_shape(F, out_dtype, nb);
+    const uint32_t threads = shape.threads;
+    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, shape.waves_per_cu);
     const int64_t tiles_per_band = (nstrips + threads - 1) / threads;
     const int64_t groups = P / 8;
     const int64_t bands = (groups + kGroupsPerThread - 1) / kGroupsPerThread;
@@ -94,7 +112,7 @@ int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_
     uint32_t a8 = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
     void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7, &a8};
     hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(bands * tiles_per_band)), dim3(threads),
-                                     args, 0, (hipStream_t)stream);
+                                     args, lds, (hipStream_t)stream);
     return err == hipSuccess ? MXQ_OK : MXQ_E_HIP;
 }
 
