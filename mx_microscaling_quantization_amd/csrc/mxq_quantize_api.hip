@@ -15,25 +15,25 @@ using mxq_host::emax_of;
 using mxq_host::kMaxF;
 using mxq_host::kMaxWorkgroups;
 
-// Workgroup width and residency. When the data rows start on 128-byte
-// lines (row pitch F bytes for FP8, F/2 for FP4, a multiple of 128),
-// single-wave workgroups stream this kernel's 2:1 read/write mix fastest,
+// Workgroups of one wave stream this kernel's 2:1 read/write mix fastest,
 // with at most 10 waves per CU once the tensor outgrows the cache (measured
 // on the 1.07 G-element bf16 -> e4m3fn input: 488 us uncapped, 473 us
-// capped). When they do not, every workgroup's first and last line of each
-// row is shared with its neighbour, and wider workgroups make those shared
-// lines rarer: 128 threads and 10 waves per CU for 2-block strips, 256
-// threads uncapped for 1-block strips (F = 8200: 729 -> 572 us; F = 8188:
-// 944 -> 609 us).
-struct LaunchShape {
-    uint32_t threads, waves_per_cu;
-};
-inline LaunchShape launch_shape(int64_t F, int out_dtype, int nb)
+// capped).
+constexpr uint32_t kThreads = 64;
+constexpr uint32_t kWavesPerCU = 10;
+
+// When the data rows do not start on 128-byte lines (row pitch F bytes for
+// FP8, F/2 for FP4, not a multiple of 128), neighbouring workgroups share
+// the first and last line of each row segment. Workgroups go to the 8 XCDs
+// round-robin, so neighbours sit behind different L2 caches and both write
+// partial lines. Renumbering the workgroups so that each XCD walks one
+// contiguous range of tiles keeps both halves of almost every shared line
+// in one L2 (F = 8200: 729 -> 538 us; F = 8188: 944 -> 582 us; aligned
+// pitches measured faster without it).
+constexpr int kXcds = 8;
+inline bool pitch_aligned(int64_t F, int out_dtype)
 {
-    const int64_t pitch = out_dtype == MXQ_OUT_E2M1 ? F / 2 : F;
-    if (pitch % 128 == 0)
-        return {64, 10};
-    return nb == 2 ? LaunchShape{128, 10} : LaunchShape{256, 0};
+    return (out_dtype == MXQ_OUT_E2M1 ? F / 2 : F) % 128 == 0;
 }
 
 typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, uint32_t, int,
@@ -44,18 +44,18 @@ typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint
 constexpr int kGroupsPerThread = 1;
 constexpr int kNonTemporal = 3;
 
-template <int IN, int OUT> kernel_fn pick_nb(int nb)
+template <int IN, int OUT, int XCD> kernel_fn pick_nb(int nb)
 {
-    return nb == 2 ? (kernel_fn)mxq::quantize_kernel<IN, OUT, 2, kGroupsPerThread, kNonTemporal>
-                   : (kernel_fn)mxq::quantize_kernel<IN, OUT, 1, kGroupsPerThread, kNonTemporal>;
+    return nb == 2 ? (kernel_fn)mxq::quantize_kernel<IN, OUT, 2, kGroupsPerThread, kNonTemporal, XCD>
+                   : (kernel_fn)mxq::quantize_kernel<IN, OUT, 1, kGroupsPerThread, kNonTemporal, XCD>;
 }
 
-template <int IN> kernel_fn pick_out(int out_dtype, int nb)
+template <int IN, int XCD> kernel_fn pick_out(int out_dtype, int nb)
 {
     switch (out_dtype) {
-    case MXQ_OUT_E4M3FN: return pick_nb<IN, mxq::kOutE4M3FN>(nb);
-    case MXQ_OUT_E5M2: return pick_nb<IN, mxq::kOutE5M2>(nb);
-    default: return pick_nb<IN, mxq::kOutE2M1>(nb);
+    case MXQ_OUT_E4M3FN: return pick_nb<IN, mxq::kOutE4M3FN, XCD>(nb);
+    case MXQ_OUT_E5M2: return pick_nb<IN, mxq::kOutE5M2, XCD>(nb);
+    default: return pick_nb<IN, mxq::kOutE2M1, XCD>(nb);
     }
 }
 
@@ -90,17 +90,18 @@ int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_
 
     const int nb = (F % 8 == 0) ? 2 : 1;
     const int64_t nstrips = F / (4 * nb);
-    const LaunchShape shape = launch_shape(F, out_dtype, nb);
-    const uint32_t threads = shape.threads;
-    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, shape.waves_per_cu);
+    const uint32_t threads = kThreads;
+    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, kWavesPerCU);
+    const bool aligned = pitch_aligned(F, out_dtype);
     const int64_t tiles_per_band = (nstrips + threads - 1) / threads;
     const int64_t groups = P / 8;
     const int64_t bands = (groups + kGroupsPerThread - 1) / kGroupsPerThread;
     if (bands > kMaxWorkgroups / tiles_per_band)
         return MXQ_E_OVERFLOW;
 
-    kernel_fn k = in_dtype == MXQ_IN_BF16 ? pick_out<mxq::kInBF16>(out_dtype, nb)
-                                          : pick_out<mxq::kInF16>(out_dtype, nb);
+    kernel_fn k = in_dtype == MXQ_IN_BF16
+                      ? (aligned ? pick_out<mxq::kInBF16, 0>(out_dtype, nb) : pick_out<mxq::kInBF16, kXcds>(out_dtype, nb))
+                      : (aligned ? pick_out<mxq::kInF16, 0>(out_dtype, nb) : pick_out<mxq::kInF16, kXcds>(out_dtype, nb));
     const uint16_t *a0 = (const uint16_t *)in;
     uint8_t *a1 = (uint8_t *)data_out;
     uint8_t *a2 = (uint8_t *)scale_out;

@@ -1,0 +1,89 @@
+"""GPU parity at extreme aspect ratios: one row group millions of columns
+wide, millions of rows a single block wide, and the axis variants' and the
+dequantize's counterparts. These stress the launch geometry (strips per row
+group, workgroups per band, 64-bit row offsets) rather than the arithmetic,
+which the other parity tests cover; every result is compared bit for bit
+with the oracle, with guard bytes after each output."""
+import numpy as np
+import pytest
+import torch
+
+import mx_microscaling_quantization_amd as mxq
+import oracle
+import workloads
+from conftest import progress
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16}
+SENTINEL = 0xA5
+GUARD = 256
+
+# (P, F): 1 row group x 2^22 + 4 columns (1-block strips, misaligned
+# pitch), 1 row group x 2^23 columns (aligned), 2^21 rows x 4 columns (one
+# strip per row group), 2^20 rows x 12 columns (three strips)
+QUANT_SHAPES = [(8, (1 << 22) + 4), (8, 1 << 23), (1 << 21, 4), (1 << 20, 12)]
+
+
+def _device(bits: np.ndarray, in_dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TDT[in_dtype]).cuda()
+
+
+@pytest.mark.parametrize("out", ["e4m3fn", "e2m1"])
+@pytest.mark.parametrize("P,F", QUANT_SHAPES)
+def test_quantize_extreme_shapes(P, F, out):
+    progress("quantize extreme %dx%d -> %s" % (P, F, out))
+    x = workloads.random_bits(P, F, "bf16", seed=P + F, specials=True)
+    nbytes = mxq.data_bytes(P, F, out)
+    buf = torch.full((nbytes + GUARD,), 0xEE, dtype=torch.uint8, device="cuda")
+    data = buf[:nbytes].view(mxq.data_shape(P, F, out))
+    sshape = mxq.scale_image_shape(P, F, False)
+    sbuf = torch.full((sshape[0] * sshape[1] + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda")
+    image = sbuf[:sshape[0] * sshape[1]].view(sshape)
+    mxq.quantize(_device(x, "bf16"), out, data_out=data, scale_out=image)
+    torch.cuda.synchronize()
+    assert bool((buf[nbytes:] == 0xEE).all()) and bool((sbuf[sshape[0] * sshape[1]:] == SENTINEL).all())
+    fill = np.full(sshape, SENTINEL, np.uint8)
+    d_ref, im_ref = oracle.quantize(x, "bf16", out, image=fill)
+    assert np.array_equal(data.cpu().numpy(), d_ref)
+    assert np.array_equal(image.cpu().numpy(), im_ref)
+
+
+@pytest.mark.parametrize("P,F", [(8, (1 << 22) + 4), (1 << 21, 4)])
+def test_dequantize_extreme_shapes(P, F):
+    progress("dequantize extreme %dx%d" % (P, F))
+    x = workloads.random_bits(P, F, "f16", seed=3 * P + F, specials=False)
+    d_ref, im_ref = oracle.quantize(x, "f16", "e5m2")
+    d = torch.from_numpy(d_ref).cuda()
+    im = torch.from_numpy(im_ref).cuda()
+    buf = torch.full((P * F + GUARD,), 7.0, dtype=torch.float32, device="cuda")
+    out = buf[:P * F].view(P, F)
+    mxq.dequantize(d, im, "e5m2", torch.float32, out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[P * F:] == 7.0).all())
+    ref = oracle.dequantize(d_ref, im_ref, P, F, "e5m2", "f32")
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# (dim, R, C): blocks along rows of a 4-row tensor 2^20 wide, along rows of
+# 2^21 + 4 rows one block wide (the row count not a multiple of 4 -> 3),
+# down the columns of a 32-row band 2^21 wide, down 2^20 rows 4 wide
+AXIS_SHAPES = [(-1, 4, 1 << 20), (-1, (1 << 21) + 3, 32), (-2, 32, 1 << 21), (-2, 1 << 20, 4)]
+
+
+@pytest.mark.parametrize("dim,R,C", AXIS_SHAPES)
+def test_quantize_axis_extreme_shapes(dim, R, C):
+    progress("quantize_axis extreme dim=%d %dx%d" % (dim, R, C))
+    x = workloads.random_bits(R, C, "bf16", seed=R + 7 * C, specials=True)
+    P, F = mxq.axis_view_shape(R, C, dim)
+    nd = mxq.data_bytes(P, F, "e4m3fn")
+    buf = torch.full((nd + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(mxq.scale_image_shape(P, F, True), dtype=torch.uint8, device="cuda")
+    mxq.quantize_axis(_device(x, "bf16"), "e4m3fn", dim, data_out=buf[:nd].view(mxq.data_shape(P, F, "e4m3fn")),
+                      scale_out=scale, dense_scale=True)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert (got[nd:] == SENTINEL).all()
+    ref_d, ref_s = oracle.quantize_axis(x, "bf16", "e4m3fn", dim, layout="dense")
+    assert np.array_equal(got[:nd].reshape(ref_d.shape), ref_d)
+    assert np.array_equal(scale.cpu().numpy(), ref_s)
