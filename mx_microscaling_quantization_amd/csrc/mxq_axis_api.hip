@@ -18,13 +18,24 @@ using mxq_host::kMaxWorkgroups;
 typedef void (*down_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, int, uint32_t);
 typedef void (*along_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint64_t, uint32_t, int, uint32_t);
 
-template <int IN, int OUT> down_kernel_fn down_pick_nb(int nb)
+// The down kernel's workgroups are renumbered so that each XCD walks one
+// contiguous range of tiles when the view rows do not start on 128-byte
+// lines, as for the plain quantize (N = 8200: 630 -> 566 us); the along
+// kernel keeps its order (renumbering it measured slower at every pitch).
+constexpr int kXcds = 8;
+
+template <int IN, int OUT, int XCD> down_kernel_fn down_pick_nb(int nb)
 {
     switch (nb) {
-    case 4: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 4>;
-    case 2: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 2>;
-    default: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 1>;
+    case 4: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 4, XCD>;
+    case 2: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 2, XCD>;
+    default: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 1, XCD>;
     }
+}
+
+template <int IN, int OUT> down_kernel_fn down_pick(int nb, bool aligned)
+{
+    return aligned ? down_pick_nb<IN, OUT, 0>(nb) : down_pick_nb<IN, OUT, kXcds>(nb);
 }
 
 template <int IN, int OUT> along_kernel_fn along_pick(int narrow)
@@ -33,19 +44,20 @@ template <int IN, int OUT> along_kernel_fn along_pick(int narrow)
                   : (along_kernel_fn)mxq::quantize_along_kernel<IN, OUT, 0>;
 }
 
-template <int IN> void axis_pick(int out_dtype, int down, int width, down_kernel_fn *d, along_kernel_fn *a)
+template <int IN>
+void axis_pick(int out_dtype, int down, int width, bool aligned, down_kernel_fn *d, along_kernel_fn *a)
 {
     switch (out_dtype) {
     case MXQ_OUT_E4M3FN:
-        *d = down ? down_pick_nb<IN, mxq::kOutE4M3FN>(width) : nullptr;
+        *d = down ? down_pick<IN, mxq::kOutE4M3FN>(width, aligned) : nullptr;
         *a = down ? nullptr : along_pick<IN, mxq::kOutE4M3FN>(width);
         break;
     case MXQ_OUT_E5M2:
-        *d = down ? down_pick_nb<IN, mxq::kOutE5M2>(width) : nullptr;
+        *d = down ? down_pick<IN, mxq::kOutE5M2>(width, aligned) : nullptr;
         *a = down ? nullptr : along_pick<IN, mxq::kOutE5M2>(width);
         break;
     default:
-        *d = down ? down_pick_nb<IN, mxq::kOutE2M1>(width) : nullptr;
+        *d = down ? down_pick<IN, mxq::kOutE2M1>(width, aligned) : nullptr;
         *a = down ? nullptr : along_pick<IN, mxq::kOutE2M1>(width);
         break;
     }
@@ -107,10 +119,11 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
     }
     down_kernel_fn dk = nullptr;
     along_kernel_fn ak = nullptr;
+    const bool aligned = (out_dtype == MXQ_OUT_E2M1 ? 2 * O : 4 * O) % 128 == 0; // view row pitch
     if (in_dtype == MXQ_IN_BF16)
-        axis_pick<mxq::kInBF16>(out_dtype, down, width, &dk, &ak);
+        axis_pick<mxq::kInBF16>(out_dtype, down, width, aligned, &dk, &ak);
     else
-        axis_pick<mxq::kInF16>(out_dtype, down, width, &dk, &ak);
+        axis_pick<mxq::kInF16>(out_dtype, down, width, aligned, &dk, &ak);
 
     const uint16_t *a0 = (const uint16_t *)in;
     uint8_t *a1 = (uint8_t *)data_out;

@@ -37,8 +37,10 @@ __device__ __forceinline__ uint32_t half16(uint32_t w, uint32_t h) { return (w >
 // the strip is NB containers: 4*NB bytes (FP8) or 2*NB (FP4) at
 // p * 4N + 4*n0 (FP8) / p * 2N + 2*n0 (FP4); the NB E8M0 bytes go to the
 // placed (or dense) scale row at column n0.
-//   nstrips   N / NB;  tiles_per_band  ceil(nstrips / 64)
-template <int IN, int OUT, int NB>
+//   nstrips   N / NB;  tiles_per_band  ceil(nstrips / 64); XCD != 0
+//   renumbers workgroups as the plain quantize does (each XCD walks one
+//   contiguous range of tiles)
+template <int IN, int OUT, int NB, int XCD = 0>
 __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__restrict__ in,
                                                            uint8_t *__restrict__ data,
                                                            uint8_t *__restrict__ scale, uint64_t N,
@@ -47,8 +49,9 @@ __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__res
 {
     static_assert(NB == 1 || NB == 2 || NB == 4, "1, 2 or 4 columns per thread");
     constexpr int NW = (NB + 1) / 2;   // loaded dwords per row
-    const uint32_t band = blockIdx.x / tiles_per_band;
-    const uint32_t strip = (blockIdx.x - band * tiles_per_band) * 64u + threadIdx.x;
+    const uint32_t tile = tile_index<XCD>();
+    const uint32_t band = tile / tiles_per_band;
+    const uint32_t strip = (tile - band * tiles_per_band) * 64u + threadIdx.x;
     if (strip >= nstrips)
         return;
     const uint64_t n0 = (uint64_t)strip * NB;

@@ -15,29 +15,31 @@ using mxq_host::kMaxF;
 using mxq_host::kMaxWorkgroups;
 
 // One 64-lane wave per workgroup, non-temporal loads and stores (the data
-// streams through once), as for the quantize.
+// streams through once), as for the quantize. When the result rows do not
+// start on 128-byte lines, workgroups are renumbered so that each XCD walks
+// one contiguous range of tiles and the lines neighbours share stay in one
+// L2, as for the quantize (F = 8200: 666 -> 565 us; F = 8188: 889 -> 581
+// us; aligned pitches are faster without it).
 constexpr uint32_t kThreads = 64;
 constexpr int kNonTemporal = 3;
+constexpr int kXcds = 8;
 
 typedef void (*dq_kernel_fn)(const uint8_t *, const uint8_t *, void *, uint64_t, uint32_t, uint32_t, uint32_t);
 
-template <int FMT, int RES> dq_kernel_fn dq_pick_nb(int nb)
+template <int FMT, int RES, int XCD> dq_kernel_fn dq_pick_nb(int nb)
 {
-    return nb == 2 ? (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 2, kNonTemporal>
-                   : (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 1, kNonTemporal>;
+    return nb == 2 ? (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 2, kNonTemporal, XCD>
+                   : (dq_kernel_fn)mxq::dequantize_kernel<FMT, RES, 1, kNonTemporal, XCD>;
 }
 
-template <int RES> dq_kernel_fn dq_pick_fmt(int fmt, int nb)
+template <int RES, int XCD> dq_kernel_fn dq_pick_fmt(int fmt, int nb)
 {
     switch (fmt) {
-    case MXQ_OUT_E4M3FN: return dq_pick_nb<mxq::kOutE4M3FN, RES>(nb);
-    case MXQ_OUT_E5M2: return dq_pick_nb<mxq::kOutE5M2, RES>(nb);
-    default: return dq_pick_nb<mxq::kOutE2M1, RES>(nb);
+    case MXQ_OUT_E4M3FN: return dq_pick_nb<mxq::kOutE4M3FN, RES, XCD>(nb);
+    case MXQ_OUT_E5M2: return dq_pick_nb<mxq::kOutE5M2, RES, XCD>(nb);
+    default: return dq_pick_nb<mxq::kOutE2M1, RES, XCD>(nb);
     }
 }
-
-// Largest normal exponent of each output format ("Block-Scale Computation",
-// The EMAX Table): the bias subtracted from a block's maximum exponent.
 
 } // namespace
 
@@ -77,8 +79,10 @@ int mxq_dequantize_ex(const void *data, const void *scale_in, int64_t P, int64_t
     if (groups > kMaxWorkgroups / tiles_per_group)
         return MXQ_E_OVERFLOW;
 
-    dq_kernel_fn k = res_dtype == MXQ_RES_F32 ? dq_pick_fmt<mxq::kResF32>(fmt, nb)
-                                              : dq_pick_fmt<mxq::kResBF16>(fmt, nb);
+    const bool aligned = F * (res_dtype == MXQ_RES_F32 ? 4 : 2) % 128 == 0; // result row pitch
+    dq_kernel_fn k = res_dtype == MXQ_RES_F32
+                         ? (aligned ? dq_pick_fmt<mxq::kResF32, 0>(fmt, nb) : dq_pick_fmt<mxq::kResF32, kXcds>(fmt, nb))
+                         : (aligned ? dq_pick_fmt<mxq::kResBF16, 0>(fmt, nb) : dq_pick_fmt<mxq::kResBF16, kXcds>(fmt, nb));
     const uint8_t *a0 = (const uint8_t *)data;
     const uint8_t *a1 = (const uint8_t *)scale_in;
     void *a2 = out;

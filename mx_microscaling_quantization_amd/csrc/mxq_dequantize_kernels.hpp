@@ -110,12 +110,13 @@ __device__ __forceinline__ void decode_block_e255(uint32_t w, uint32_t *out)
 }
 
 // The dequantize kernel. Grid as the quantize (GPT = 1): one workgroup per
-// (row group, run of blockDim.x strips).
+// (row group, run of blockDim.x strips); XCD != 0 renumbers workgroups as
+// the quantize does, so each XCD walks one contiguous range of tiles.
 //   data    FP8: P*F bytes; FP4: P*F/2 bytes
 //   scale   the P x F/4 scale image (only the placed rows are read), or with
 //           dense = 1 the [P/8, F/4] scale array
 //   out     P x F results, fp32 or bf16
-template <int FMT, int RES, int NB, int NT>
+template <int FMT, int RES, int NB, int NT, int XCD = 0>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restrict__ data,
                                                          const uint8_t *__restrict__ scale,
                                                          void *__restrict__ out, uint64_t F,
@@ -125,8 +126,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
     static_assert(NB == 1 || NB == 2, "a strip is 1 or 2 blocks");
     constexpr int LD = NT & 1, ST = (NT >> 1) & 1;
     constexpr int RES_BYTES = RES == kResF32 ? 4 : 2;
-    const uint32_t group = blockIdx.x / tiles_per_band;
-    const uint32_t strip = (blockIdx.x - group * tiles_per_band) * blockDim.x + threadIdx.x;
+    const uint32_t tile = tile_index<XCD>();
+    const uint32_t group = tile / tiles_per_band;
+    const uint32_t strip = (tile - group * tiles_per_band) * blockDim.x + threadIdx.x;
     if (strip >= nstrips)
         return;
 
