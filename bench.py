@@ -35,6 +35,12 @@ per step as the quantize).
 in the kernel's epilogue (format ``--out``, default e4m3fn), and reports the
 unfused pair (bf16 matmul, then quantize) on the same operands beside it.
 
+With the CPU baseline on (the default), the quantize line carries two
+figures for the oracle on the same input: ``cpu_baseline`` (one thread on
+leading row slabs, about 12 s of oracle time) and ``cpu_baseline_all_cores``
+(the whole tensor split into whole 32-row bands over up to 16 threads,
+wall-clock time).
+
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
 WRITE_SIZE readings into bytes.
@@ -155,6 +161,38 @@ def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows:
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "first %d of %d rows (%d x %d, %.3g s of single-thread oracle time)"
                       % (done_rows, P, done_rows, F, spent)}
+
+
+def cpu_baseline_all_cores(xt, out: str, in_dtype: str, max_threads: int = 16):
+    """The same CPU oracle, unchanged, on every host core the run may use
+    (at most max_threads): the whole input split into one slab of whole
+    32-row bands per thread, each slab quantized by its own call (ctypes
+    releases the interpreter lock during the call). Wall-clock time."""
+    import concurrent.futures
+
+    import numpy as np
+    import torch
+
+    import oracle
+
+    oracle.build(force=False)
+    oracle.quantize(np.zeros((8, 4), np.uint16), in_dtype, out)   # load the library before the threads
+    P, F = xt.shape
+    host = xt.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    n = max(1, min(max_threads, os.cpu_count() or 1, P // 32))
+    bands = P // 32
+    cuts = [32 * (bands * t // n) for t in range(n)] + [P]
+
+    def work(t):
+        oracle.quantize(host[cuts[t]:cuts[t + 1]], in_dtype, out)
+
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(n) as ex:
+        list(ex.map(work, range(n)))
+    spent = time.perf_counter() - t0
+    return {"value": round(algorithmic_bytes(P, F, out) / spent / 1e9, 4), "unit": "GB/s", "cores": n,
+            "kind": "oracle",
+            "sample": "all %d rows (%d x %d) in %d slabs on %d threads, %.3g s wall" % (P, P, F, n, n, spent)}
 
 
 def cpu_baseline_dequant(data, image, fmt: str, res: str, budget_s: float = 12.0, slab_rows: int = 4096):
@@ -453,6 +491,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         if args.op == "quantize":
             result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"])
+            result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(xt, out, spec["in_dtype"])
         elif args.op == "quantize_axis":
             result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"], dim=args.dim)
         else:
