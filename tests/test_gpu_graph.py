@@ -47,3 +47,55 @@ def test_graph_capture_and_replay():
         assert torch.equal(back.view(torch.int16), b_ref.view(torch.int16)), "replay %d dequantize" % rep
         # unrelated eager work between replays
         _ = (xt.float() * 2).sum().item()
+
+
+def test_graph_capture_every_entry_point():
+    """Axis quantize (both axes), scaled matmul, quantize-on-produce and a
+    quantize large enough for the occupancy-capped launch (its traffic
+    exceeds the cache, so the launch reserves LDS): all captured in one
+    graph, every replay equal to the eager results."""
+    g_ = torch.Generator(device="cuda")
+    g_.manual_seed(11)
+    big = torch.randn((8192, 16384), generator=g_, device="cuda").to(torch.bfloat16)
+    X = torch.randn((264, 512), generator=g_, device="cuda").to(torch.bfloat16)
+    W = torch.randn((512, 136), generator=g_, device="cuda").to(torch.bfloat16)
+
+    def run(outs=None):
+        o = outs or {}
+        d_big, s_big = mxq.quantize(big, "e4m3fn", data_out=o.get("d_big"), scale_out=o.get("s_big"))
+        dl, sl = mxq.quantize_axis(X, "e4m3fn", -1, data_out=o.get("dl"), scale_out=o.get("sl"))
+        dr, sr = mxq.quantize_axis(W, "e4m3fn", -2, data_out=o.get("dr"), scale_out=o.get("sr"))
+        mm = mxq.scaled_matmul(dl, sl, dr, sr, "e4m3fn", torch.float32, out=o.get("mm"))
+        qd, qs = mxq.scaled_matmul_quantize(dl, sl, dr, sr, "e4m3fn", "e4m3fn", data_out=o.get("qd"),
+                                            scale_out=o.get("qs"))
+        return {"d_big": d_big, "s_big": s_big, "dl": dl, "sl": sl, "dr": dr, "sr": sr, "mm": mm, "qd": qd,
+                "qs": qs}
+
+    ref = {k: v.clone() for k, v in run().items()}
+    torch.cuda.synchronize()
+    bufs = {k: torch.zeros_like(v) for k, v in ref.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(bufs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(bufs)
+    for rep in range(4):
+        for v in bufs.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ("d_big", "dl", "dr", "qd"):
+            assert torch.equal(bufs[k], ref[k]), "replay %d: %s" % (rep, k)
+        assert torch.equal(bufs["mm"].view(torch.int32), ref["mm"].view(torch.int32)), "replay %d: matmul" % rep
+        # scale images: compare the placed rows (the others are never written)
+        for k in ("s_big", "sl", "sr", "qs"):
+            P = bufs[k].shape[0]
+            rows = torch.tensor([(i % 4) + 32 * (i // 4) for i in range(P // 8)], device="cuda")
+            assert torch.equal(bufs[k][rows], ref[k][rows]), "replay %d: %s" % (rep, k)
+        _ = (X.float() * 2).sum().item()
