@@ -319,6 +319,7 @@ def bench_matmul(args) -> int:
             mxq.scaled_matmul(dl, sl, dr, sr, fmt, res_t, out=out, stream=stream)
 
     total_ms, avg_ms = _time_steps(step, args.steps, args.warmup, stream)
+    traffic = recorded_traffic("%s-%dx%dx%d" % (fmt, M, N, K), qout if fused else args.res, args.op)
     flops = 2.0 * M * N * K
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
@@ -329,7 +330,7 @@ def bench_matmul(args) -> int:
         "config": {"workload": "%s-%dx%dx%d-scaled-matmul%s" % (fmt, M, N, K, "-quantized-%s" % qout if fused else ""),
                    "M": M, "N": N, "K": K, "out": qout if fused else args.res, "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel_avg_us": round(avg_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
