@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--op quantize|dequantize|matmul|matmul_quantize|quantize_axis]
-                    [--dim -1|-2] [--res bf16|f32]
+                    [--dim -1|-2] [--res bf16|f32] [--cache hot|flushed]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one full quantize of the workload tensor (one kernel launch: block
@@ -40,6 +40,13 @@ figures for the oracle on the same input: ``cpu_baseline`` (one thread on
 leading row slabs, about 12 s of oracle time) and ``cpu_baseline_all_cores``
 (the whole tensor split into whole 32-row bands over up to 16 threads,
 wall-clock time).
+
+``--cache flushed`` (streaming ops) reads a 512 MiB buffer, twice the
+Infinity Cache, before every launch, so no launch finds its operands cached;
+``value`` and ``ms_per_step`` then cover the launches alone (the sum of the
+per-launch events), not the flushes between them. The default, ``hot``,
+runs the launches back to back on the same buffers: a workload under the
+cache size is then served largely from the cache.
 
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
@@ -376,6 +383,8 @@ def main() -> int:
     ap.add_argument("--mm", type=int, nargs=3, default=(8192, 8192, 8192), metavar=("M", "N", "K"),
                     help="matmul sizes (M, N multiples of 4, K a multiple of 32)")
     ap.add_argument("--res", choices=("bf16", "f32"), default="bf16", help="dequantize result type")
+    ap.add_argument("--cache", choices=("hot", "flushed"), default="hot",
+                    help="flushed: write 512 MiB between launches and time the launches alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -432,6 +441,20 @@ def main() -> int:
             mxq.dequantize(data, image, out, res_t, out=result, stream=stream)
         nbytes = dequant_bytes(P, F, out, args.res)
 
+    flushed = args.cache == "flushed"
+    if flushed:
+        # a read of twice the Infinity Cache's size between launches, so each
+        # launch finds none of its operands cached; a read leaves the caches
+        # clean (a write would leave dirty lines whose write-back lands in
+        # the next launch); it runs outside the per-launch events, and value
+        # then counts the launches only
+        flush_buf = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+        timed_step = step
+
+        def step():
+            flush_buf.sum()
+            return timed_step()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -442,8 +465,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t_begin.record(stream)
     for k in range(args.steps):
+        if flushed:
+            flush_buf.sum()
         starts[k].record(stream)
-        step()
+        (timed_step if flushed else step)()
         ends[k].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -451,6 +476,8 @@ def main() -> int:
     total_ms = t_begin.elapsed_time(t_end)
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    if flushed:
+        total_ms = sum(per_launch_ms)
     value = nbytes * args.steps / (total_ms * 1e-3) / 1e9
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
     if args.op == "quantize":
@@ -462,6 +489,8 @@ def main() -> int:
 
     config = {"workload": args.workload, "P": P, "F": F, "in": spec["in_dtype"], "out": out,
               "bytes_per_step": nbytes, "elements_per_step": P * F}
+    if flushed:
+        config["cache"] = "flushed"
     if args.op == "quantize_axis":
         config = {"workload": "%s-axis%d" % (args.workload, args.dim), "R": P, "C": F, "dim": args.dim,
                   "in": spec["in_dtype"], "out": out, "bytes_per_step": nbytes, "elements_per_step": P * F}
