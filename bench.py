@@ -142,6 +142,26 @@ def make_input(workload: str, device):
     return xt, spec
 
 
+def host_cpu() -> dict:
+    """The host the CPU baselines ran on: its processor model (from
+    /proc/cpuinfo), the logical CPUs it reports and the ones this process
+    may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count() or 1, "usable_cpus": usable}
+
+
 def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows: int = 4096, dim: int | None = None):
     """The CPU oracle (single thread, as it stands) on leading row slabs of
     the same input until about budget_s seconds of oracle time (with dim,
@@ -166,6 +186,7 @@ def cpu_baseline(xt, out: str, in_dtype: str, budget_s: float = 12.0, slab_rows:
         done_rows += rows
     nbytes = algorithmic_bytes(done_rows, F, out)
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host": host_cpu(),
             "sample": "first %d of %d rows (%d x %d, %.3g s of single-thread oracle time)"
                       % (done_rows, P, done_rows, F, spent)}
 
@@ -198,7 +219,7 @@ def cpu_baseline_all_cores(xt, out: str, in_dtype: str, max_threads: int = 16):
         list(ex.map(work, range(n)))
     spent = time.perf_counter() - t0
     return {"value": round(algorithmic_bytes(P, F, out) / spent / 1e9, 4), "unit": "GB/s", "cores": n,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": "all %d rows (%d x %d) in %d slabs on %d threads, %.3g s wall" % (P, P, F, n, n, spent)}
 
 
@@ -220,6 +241,7 @@ def cpu_baseline_dequant(data, image, fmt: str, res: str, budget_s: float = 12.0
         done_rows += rows
     nbytes = dequant_bytes(done_rows, F, fmt, res)
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host": host_cpu(),
             "sample": "first %d of %d rows (%d x %d, %.3g s of single-thread oracle time)"
                       % (done_rows, P, done_rows, F, spent)}
 
@@ -253,6 +275,7 @@ def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block:
         done += 1
     flops = 2.0 * done * block * block * 4 * P
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "host": host_cpu(),
             "sample": "%d diagonal %dx%d output tiles at K=%d (%.3g s of single-thread oracle time)"
                       % (done, block, block, 4 * P, spent)}
 

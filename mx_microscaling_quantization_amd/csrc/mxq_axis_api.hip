@@ -16,12 +16,18 @@ using mxq_host::kMaxF;
 using mxq_host::kMaxWorkgroups;
 
 typedef void (*down_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, int, uint32_t);
-typedef void (*along_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint64_t, uint32_t, int, uint32_t);
+typedef void (*along_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint64_t, uint32_t, int, uint32_t,
+                                uint32_t);
 
 // The down kernel's workgroups are renumbered so that each XCD walks one
 // contiguous range of tiles when the view rows do not start on 128-byte
-// lines, as for the plain quantize (N = 8200: 630 -> 566 us); the along
-// kernel keeps its order (renumbering it measured slower at every pitch).
+// lines, as for the plain quantize (N = 8200: 630 -> 566 us). The along
+// kernel slows down under that renumbering at every pitch; instead, when
+// the row count is not a multiple of its 256-row tile (so its view-row runs
+// do not start on run-size boundaries), each XCD takes four adjacent row
+// tiles of every window of 32 workgroups. 8192 columns, bf16 -> e4m3fn:
+// 131080 rows 621 -> 593 us, 131074 672 -> 631 us, 131040 593 -> 565 us;
+// multiples of 256 rows are as fast or faster without it (131072: 545 us).
 constexpr int kXcds = 8;
 
 template <int IN, int OUT, int XCD> down_kernel_fn down_pick_nb(int nb)
@@ -144,7 +150,8 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
     } else {
         uint64_t a3 = (uint64_t)O, a4 = (uint64_t)K;
         uint32_t a5 = (uint32_t)tiles;
-        void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7};
+        uint32_t a8 = O % mxq::kAlongRows != 0 ? 1u : 0u;
+        void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7, &a8};
         err = hipLaunchKernel((const void *)ak, dim3((uint32_t)grid), dim3(64 * mxq::kAlongWaves), args, 0,
                               (hipStream_t)stream);
     }

@@ -166,7 +166,11 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t x)
 //    (M % 4 != 0: view rows are not 16-byte aligned) every lane stores one
 //    row: 4 or 2 code bytes and 1 scale byte.
 // Row tiles vary fastest over the grid (ceil(M / kAlongRows) x ceil(K / 64)),
-// so the workgroups in flight write few view rows, each in long runs.
+// so the workgroups in flight write few view rows, each in long runs. With
+// `chunked` each full window of 32 workgroups is renumbered so that the XCD
+// receiving workgroups x, x + 8, x + 16 and x + 24 of it (they are dealt out
+// round-robin) handles row tiles 4x .. 4x + 3 of the window: adjacent runs,
+// and most lines at run boundaries, then stay behind one L2.
 constexpr uint32_t kAlongWaves = 2;
 constexpr uint32_t kAlongWaveRows = 128;
 constexpr uint32_t kAlongRows = kAlongWaves * kAlongWaveRows;
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(64 * kAlongWaves) void quantize_along_kernel(const 
                                                                           uint8_t *__restrict__ data,
                                                                           uint8_t *__restrict__ scale, uint64_t M,
                                                                           uint64_t K, uint32_t tiles_m, int emax_bias,
-                                                                          uint32_t dense)
+                                                                          uint32_t dense, uint32_t chunked)
 {
     constexpr uint32_t RT = kAlongRows, KG = kAlongWaveRows / 32; // four-load groups per lane
     constexpr uint32_t CB = OUT == kOutE2M1 ? 2 : 4;              // code bytes per row and view row
@@ -187,8 +191,11 @@ __global__ __launch_bounds__(64 * kAlongWaves) void quantize_along_kernel(const 
 
     const uint32_t t = threadIdx.x, w = t >> 6, l = t & 63u;
     const uint32_t c = l & 7u, i = l >> 3, q = c & 3u, bl = c >> 2;
-    const uint32_t tk = blockIdx.x / tiles_m;
-    const uint64_t m0 = (uint64_t)(blockIdx.x - tk * tiles_m) * RT;
+    uint32_t tile = blockIdx.x;
+    if (chunked && tile < gridDim.x / 32u * 32u)
+        tile = (tile & ~31u) | (tile & 7u) << 2 | (tile >> 3 & 3u);
+    const uint32_t tk = tile / tiles_m;
+    const uint64_t m0 = (uint64_t)(tile - tk * tiles_m) * RT;
     const uint64_t G = K / 32;
     const uint64_t g = (uint64_t)tk * 2u + bl;
 

@@ -57,10 +57,13 @@ def run(bits, in_dtype, fmt, dim, alt=False, dense=False):
 
 # dim -1 rows (R) cover both store widths (R % 4 == 0: 16/8-byte stores; else
 # one row per lane), partial 256-row tiles and odd block counts (C/32 odd:
-# the last tile holds one block)
+# the last tile holds one block); the last three have grids of 272, 90 and
+# 102 workgroups with R % 256 != 0, so whole 32-workgroup windows are
+# renumbered and a tail is not
 SHAPES = [(-2, 32, 4), (-2, 64, 36), (-2, 96, 64), (-2, 128, 130), (-2, 256, 257), (-2, 1024, 1000),
           (-1, 13, 96), (-1, 64, 64), (-1, 100, 256), (-1, 1000, 512), (-1, 7, 32), (1, 70, 160), (0, 160, 70),
-          (-1, 4, 32), (-1, 260, 96), (-1, 516, 1056), (-1, 1001, 160), (-1, 256, 64)]
+          (-1, 4, 32), (-1, 260, 96), (-1, 516, 1056), (-1, 1001, 160), (-1, 256, 64),
+          (-1, 4100, 1024), (-1, 2050, 640), (-1, 4104, 352)]
 
 
 @pytest.mark.parametrize("in_dtype,fmt", [("bf16", "e4m3fn"), ("bf16", "e5m2"), ("bf16", "e2m1"),
