@@ -16,9 +16,9 @@ import threading
 import torch  # loaded first so that the library binds to torch's HIP runtime
 
 __all__ = [
-    "IN_DTYPES", "OUT_DTYPES", "RES_DTYPES", "MXQError", "quantize", "dequantize", "scaled_matmul", "data_bytes",
-    "scale_image_bytes", "result_bytes", "data_shape", "scale_image_shape", "logical_scale_view",
-    "status_string", "library_path", "load",
+    "IN_DTYPES", "OUT_DTYPES", "RES_DTYPES", "MXQError", "quantize", "dequantize", "quantize_axis", "scaled_matmul",
+    "scaled_matmul_quantize", "data_bytes", "scale_image_bytes", "result_bytes", "data_shape", "scale_image_shape",
+    "axis_view_shape", "logical_scale_view", "status_string", "library_path", "load",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -114,6 +114,13 @@ def _out_code(out_dtype: str) -> int:
         raise MXQError(2, "output element type must be one of %s" % sorted(OUT_DTYPES)) from None
 
 
+def _check_out_buffer(name: str, t: torch.Tensor, nbytes: int, device: torch.device) -> None:
+    """An output the library writes through a raw pointer: contiguous, on
+    ``device``, and at least ``nbytes`` long (its element type is not read)."""
+    if t.device != device or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s must be a contiguous buffer of >= %d bytes on %s" % (name, nbytes, device))
+
+
 def data_bytes(P: int, F: int, out_dtype: str) -> int:
     return int(load().mxq_data_bytes(P, F, _out_code(out_dtype)))
 
@@ -175,10 +182,8 @@ def quantize(x: torch.Tensor, out_dtype: str = "e4m3fn", data_out: torch.Tensor 
     flags = (FLAG_ALT_EMAX if alt_emax else 0) | (FLAG_DENSE_SCALE if dense_scale else 0)
     if scale_out is None:
         scale_out = torch.empty(scale_image_shape(P, F, dense_scale), dtype=torch.uint8, device=x.device)
-    for name, t, nbytes in (("data_out", data_out, lib.mxq_data_bytes(P, F, code)),
-                            ("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags))):
-        if t.device != x.device or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
-            raise ValueError("%s must be a contiguous buffer of >= %d bytes on %s" % (name, nbytes, x.device))
+    _check_out_buffer("data_out", data_out, lib.mxq_data_bytes(P, F, code), x.device)
+    _check_out_buffer("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags), x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
@@ -208,6 +213,8 @@ def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "
         raise ValueError("data and scale_image must be device tensors on one device")
     if not (data.is_contiguous() and scale_image.is_contiguous()):
         raise ValueError("data and scale_image must be contiguous")
+    if data.dtype != torch.uint8 or scale_image.dtype != torch.uint8:
+        raise ValueError("data and scale_image must be uint8 (the bytes quantize wrote)")
     P = data.shape[0]
     F = scale_image.shape[1] * 4
     if tuple(data.shape) != data_shape(P, F, out_dtype) or \
@@ -226,6 +233,20 @@ def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "
     return out
 
 
+def _check_operands(lhs, lhs_scale, rhs, rhs_scale, dense_scale):
+    for t in (lhs, lhs_scale, rhs, rhs_scale):
+        if t.dim() != 2 or t.dtype != torch.uint8 or not t.is_contiguous() or t.device != lhs.device or not t.is_cuda:
+            raise ValueError("operands must be contiguous 2-D uint8 device tensors on one device")
+    P = lhs.shape[0]
+    M, N = lhs.shape[1] // 4, rhs.shape[1] // 4
+    if rhs.shape[0] != P or lhs.shape[1] % 4 or rhs.shape[1] % 4:
+        raise ValueError("lhs [P, 4M] and rhs [P, 4N] must share P")
+    if tuple(lhs_scale.shape) != scale_image_shape(P, 4 * M, dense_scale) or \
+            tuple(rhs_scale.shape) != scale_image_shape(P, 4 * N, dense_scale):
+        raise ValueError("scale shapes do not match the operands")
+    return P, M, N
+
+
 def scaled_matmul(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor, rhs_scale: torch.Tensor,
                   fmt: str = "e4m3fn", res_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None,
                   stream: torch.cuda.Stream | None = None, dense_scale: bool = False) -> torch.Tensor:
@@ -242,16 +263,7 @@ def scaled_matmul(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor,
     code = _out_code(fmt)
     if res_dtype not in RES_DTYPES:
         raise MXQError(10, "result type must be float32 or bfloat16, got %s" % res_dtype)
-    for t in (lhs, lhs_scale, rhs, rhs_scale):
-        if t.dim() != 2 or t.dtype != torch.uint8 or not t.is_contiguous() or t.device != lhs.device or not t.is_cuda:
-            raise ValueError("operands must be contiguous 2-D uint8 device tensors on one device")
-    P = lhs.shape[0]
-    M, N = lhs.shape[1] // 4, rhs.shape[1] // 4
-    if rhs.shape[0] != P or lhs.shape[1] % 4 or rhs.shape[1] % 4:
-        raise ValueError("lhs [P, 4M] and rhs [P, 4N] must share P")
-    if tuple(lhs_scale.shape) != scale_image_shape(P, 4 * M, dense_scale) or \
-            tuple(rhs_scale.shape) != scale_image_shape(P, 4 * N, dense_scale):
-        raise ValueError("scale shapes do not match the operands")
+    P, M, N = _check_operands(lhs, lhs_scale, rhs, rhs_scale, dense_scale)
     if out is None:
         out = torch.empty((M, N), dtype=res_dtype, device=lhs.device)
     elif out.dtype != res_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous() or out.device != lhs.device:
@@ -263,20 +275,6 @@ def scaled_matmul(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor,
                                      code, RES_DTYPES[res_dtype], FLAG_DENSE_SCALE if dense_scale else 0,
                                      out.data_ptr(), stream.cuda_stream))
     return out
-
-
-def _check_operands(lhs, lhs_scale, rhs, rhs_scale, dense_scale):
-    for t in (lhs, lhs_scale, rhs, rhs_scale):
-        if t.dim() != 2 or t.dtype != torch.uint8 or not t.is_contiguous() or t.device != lhs.device or not t.is_cuda:
-            raise ValueError("operands must be contiguous 2-D uint8 device tensors on one device")
-    P = lhs.shape[0]
-    M, N = lhs.shape[1] // 4, rhs.shape[1] // 4
-    if rhs.shape[0] != P or lhs.shape[1] % 4 or rhs.shape[1] % 4:
-        raise ValueError("lhs [P, 4M] and rhs [P, 4N] must share P")
-    if tuple(lhs_scale.shape) != scale_image_shape(P, 4 * M, dense_scale) or \
-            tuple(rhs_scale.shape) != scale_image_shape(P, 4 * N, dense_scale):
-        raise ValueError("scale shapes do not match the operands")
-    return P, M, N
 
 
 def scaled_matmul_quantize(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor, rhs_scale: torch.Tensor,
@@ -302,10 +300,8 @@ def scaled_matmul_quantize(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torc
         data_out = torch.empty(data_shape(M, N, out_dtype), dtype=torch.uint8, device=lhs.device)
     if scale_out is None:
         scale_out = torch.empty(scale_image_shape(M, N, dense_scale), dtype=torch.uint8, device=lhs.device)
-    for name, t, nbytes in (("data_out", data_out, lib.mxq_data_bytes(M, N, out_code)),
-                            ("scale_out", scale_out, lib.mxq_scale_bytes(M, N, flags))):
-        if t.dtype != torch.uint8 or not t.is_contiguous() or t.device != lhs.device or t.numel() != nbytes:
-            raise ValueError("%s must be a contiguous uint8 tensor of %d bytes on %s" % (name, nbytes, lhs.device))
+    _check_out_buffer("data_out", data_out, lib.mxq_data_bytes(M, N, out_code), lhs.device)
+    _check_out_buffer("scale_out", scale_out, lib.mxq_scale_bytes(M, N, flags), lhs.device)
     if stream is None:
         stream = torch.cuda.current_stream(lhs.device)
     with torch.cuda.device(lhs.device):
@@ -349,10 +345,8 @@ def quantize_axis(x: torch.Tensor, out_dtype: str = "e4m3fn", dim: int = -1, dat
         data_out = torch.empty(data_shape(P, F, out_dtype), dtype=torch.uint8, device=x.device)
     if scale_out is None:
         scale_out = torch.empty(scale_image_shape(P, F, dense_scale), dtype=torch.uint8, device=x.device)
-    for name, t, nbytes in (("data_out", data_out, lib.mxq_data_bytes(P, F, code)),
-                            ("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags))):
-        if t.device != x.device or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
-            raise ValueError("%s must be a contiguous buffer of >= %d bytes on %s" % (name, nbytes, x.device))
+    _check_out_buffer("data_out", data_out, lib.mxq_data_bytes(P, F, code), x.device)
+    _check_out_buffer("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags), x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):

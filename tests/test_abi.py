@@ -263,3 +263,33 @@ def test_library_does_not_link_the_oracle():
     assert "oracle" not in out
     deps = os.popen("readelf -d %s" % mxq.library_path()).read()
     assert "oracle" not in deps
+
+
+def test_binding_exports_what_it_lists():
+    assert [n for n in mxq.__all__ if not hasattr(mxq, n)] == []
+    for n in ("quantize", "dequantize", "quantize_axis", "scaled_matmul", "scaled_matmul_quantize"):
+        assert n in mxq.__all__
+
+
+def test_binding_axis_and_shape_helpers():
+    assert mxq.axis_view_shape(100, 64, -1) == (16, 400)      # blocks along rows: K = C
+    assert mxq.axis_view_shape(64, 100, -2) == (16, 400)      # blocks down columns: K = R
+    assert mxq.axis_view_shape(64, 100, 0) == mxq.axis_view_shape(64, 100, -2)
+    with pytest.raises(mxq.MXQError) as ei:
+        mxq.axis_view_shape(64, 100, 2)
+    assert ei.value.status == 11
+    assert mxq.data_shape(16, 400, "e2m1") == (16, 200)
+    assert mxq.scale_image_shape(16, 400) == (16, 100)
+    assert mxq.scale_image_shape(16, 400, dense_scale=True) == (2, 100)
+
+
+def test_binding_rejects_host_tensors_everywhere():
+    import torch
+
+    u8 = torch.zeros(8, 16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mxq.dequantize(u8, torch.zeros(8, 4, dtype=torch.uint8), "e4m3fn")
+    with pytest.raises(ValueError):
+        mxq.scaled_matmul(u8, torch.zeros(8, 4, dtype=torch.uint8), u8, torch.zeros(8, 4, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        mxq.quantize_axis(torch.zeros(8, 32, dtype=torch.bfloat16), "e4m3fn", -1)
