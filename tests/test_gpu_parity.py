@@ -235,3 +235,40 @@ def test_outputs_on_caller_stream():
     s.synchronize()
     d_ref, _ = oracle.quantize(x, "f16", "e5m2")
     assert np.array_equal(d.cpu().numpy(), d_ref)
+
+
+def test_concurrent_host_threads():
+    """The library keeps no state: host threads calling it at the same time,
+    each on its own stream, get the bytes a serial call gives."""
+    import concurrent.futures
+
+    cases = [(workloads.random_bits(256 + 64 * k, 1024, "bf16", seed=40 + k, specials=True), out)
+             for k, out in enumerate(("e4m3fn", "e5m2", "e2m1", "e4m3fn"))]
+    inputs = [(to_device(x, "bf16"), out) for x, out in cases]
+    serial = []
+    for xt, out in inputs:
+        d, im = mxq.quantize(xt, out)
+        torch.cuda.synchronize()
+        serial.append((d.cpu().numpy(), im.cpu().numpy()))
+    progress("quantize from 4 host threads, 4 streams, 8 rounds")
+
+    def work(k):
+        xt, out = inputs[k]
+        s = torch.cuda.Stream()
+        got = []
+        for _ in range(8):
+            with torch.cuda.stream(s):
+                d, im = mxq.quantize(xt, out, stream=s)
+            got.append((d, im))
+        s.synchronize()
+        return [(d.cpu().numpy(), im.cpu().numpy()) for d, im in got]
+
+    with concurrent.futures.ThreadPoolExecutor(4) as ex:
+        results = list(ex.map(work, range(4)))
+    for k, rounds in enumerate(results):
+        for d, im in rounds:
+            assert np.array_equal(d, serial[k][0])
+            # only the placed rows are defined (the image was allocated empty)
+            P = inputs[k][0].shape[0]
+            placed = (np.arange(P // 8) % 4) + 32 * (np.arange(P // 8) // 4)
+            assert np.array_equal(im[placed], serial[k][1][placed])
