@@ -10,8 +10,10 @@ A step is one full quantize of the workload tensor (one kernel launch: block
 scales, prescale, narrow, packing and scale placement). The input is
 generated on the device before timing and stays resident in HBM. The timed
 region is K back-to-back steps on one stream, bracketed by device
-synchronisation; every launch is also bracketed by its own pair of HIP events
-on that stream, which gives the kernel's average duration for the roofline.
+synchronisation and by two HIP events on that stream; with one launch per
+step, the span over K is also the kernel's average launch duration for the
+roofline. (An event pair around every launch would add about 7 us per step
+to a 475 us quantize.)
 
 Prints one JSON line. ``value`` is algorithmic GB/s over the timed region:
 bytes per step = input (2 B/element) + data (1 B/element FP8, 0.5 B FP4) +
@@ -43,8 +45,9 @@ wall-clock time).
 
 ``--cache flushed`` (streaming ops) reads a 512 MiB buffer, twice the
 Infinity Cache, before every launch, so no launch finds its operands cached;
-``value`` and ``ms_per_step`` then cover the launches alone (the sum of the
-per-launch events), not the flushes between them. The default, ``hot``,
+each launch then gets its own pair of HIP events, and ``value`` and
+``ms_per_step`` cover the launches alone (the sum of those spans), not the
+flushes between them. The default, ``hot``,
 runs the launches back to back on the same buffers: a workload under the
 cache size is then served largely from the cache.
 
@@ -280,26 +283,41 @@ def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block:
                       % (done, block, block, 4 * P, spent)}
 
 
-def _time_steps(step, steps: int, warmup: int, stream):
-    """Per-launch HIP events on `stream` around each step, plus the span."""
+def _time_steps(step, steps: int, warmup: int, stream, pre=None):
+    """Time `steps` calls of `step` on `stream` after `warmup` untimed ones.
+
+    Without `pre` the steps run back to back between two HIP events, and the
+    span over `steps` is both the step time and, one launch per step, the
+    kernel's average launch duration. With `pre` (work that must not be
+    timed, such as a cache flush) `pre()` runs before every step, and each
+    step gets its own pair of events: the total is the sum of those spans.
+    Returns (total_ms, avg_ms)."""
     import torch
 
     for _ in range(warmup):
+        if pre is not None:
+            pre()
         step()
     torch.cuda.synchronize()
+    if pre is None:
+        t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_begin.record(stream)
+        for _ in range(steps):
+            step()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_begin.elapsed_time(t_end)
+        return total_ms, total_ms / steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_begin.record(stream)
     for k in range(steps):
+        pre()
         starts[k].record(stream)
         step()
         ends[k].record(stream)
-    t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    avg_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
-    return total_ms, avg_ms
+    total_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return total_ms, total_ms / steps
 
 
 def bench_matmul(args) -> int:
@@ -465,42 +483,18 @@ def main() -> int:
         nbytes = dequant_bytes(P, F, out, args.res)
 
     flushed = args.cache == "flushed"
+    flush = None
     if flushed:
-        # a read of twice the Infinity Cache's size between launches, so each
+        # a read of twice the Infinity Cache's size before each launch, so the
         # launch finds none of its operands cached; a read leaves the caches
         # clean (a write would leave dirty lines whose write-back lands in
-        # the next launch); it runs outside the per-launch events, and value
-        # then counts the launches only
+        # the next launch); it stays outside the timed spans
         flush_buf = torch.ones(64 << 20, dtype=torch.int64, device=dev)
-        timed_step = step
 
-        def step():
+        def flush():
             flush_buf.sum()
-            return timed_step()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for k in range(args.steps):
-        if flushed:
-            flush_buf.sum()
-        starts[k].record(stream)
-        (timed_step if flushed else step)()
-        ends[k].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-
-    total_ms = t_begin.elapsed_time(t_end)
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
-    if flushed:
-        total_ms = sum(per_launch_ms)
+    total_ms, avg_launch_ms = _time_steps(step, args.steps, args.warmup, stream, pre=flush)
     value = nbytes * args.steps / (total_ms * 1e-3) / 1e9
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
     if args.op == "quantize":
