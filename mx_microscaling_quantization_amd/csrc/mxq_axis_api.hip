@@ -142,9 +142,12 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
         uint32_t a4 = (uint32_t)(O / width), a5 = (uint32_t)tiles;
         void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6, &a7};
         // at most 8 waves per CU once the tensor outgrows the cache (1.07 G
-        // elements: 514 us uncapped, 487 us capped); the along kernel's own
-        // LDS tile already sets its residency, and more reserve slows it
-        const uint32_t lds = mxq_host::occupancy_cap_lds(K * O, 3, (uint32_t)threads, 8);
+        // elements: 514 us uncapped, 487 us capped), 12 for one-column
+        // strips, whose threads move a quarter of the bytes (32768 x 32769:
+        // 746 us at 8, 665 us at 12; two- and four-column strips are fastest
+        // at 8); the along kernel's own LDS tile already sets its residency,
+        // and more reserve slows it
+        const uint32_t lds = mxq_host::occupancy_cap_lds(K * O, 3, (uint32_t)threads, width == 1 ? 12 : 8);
         err = hipLaunchKernel((const void *)dk, dim3((uint32_t)grid), dim3((uint32_t)threads), args, lds,
                               (hipStream_t)stream);
     } else {

@@ -19,9 +19,16 @@ using mxq_host::kMaxWorkgroups;
 // once the tensor outgrows the cache: at most 10 waves per CU for FP8 output
 // (2:1 read/write; 1.07 G-element bf16 -> e4m3fn: 488 us uncapped, 473 us
 // capped) and 8 for FP4 output (4:1; -> e2m1: 434 us uncapped, 414 us at 10,
-// 391 us at 8).
+// 391 us at 8). A thread of one-block strips (F % 8 == 4) moves half the
+// bytes, so 12 waves keep as much in flight (131072 x 8188: -> e4m3fn 549 us
+// at 10, 535 us at 12; -> e2m1 529 us at 8, 437 us at 12).
 constexpr uint32_t kThreads = 64;
-inline uint32_t waves_per_cu(int out_dtype) { return out_dtype == MXQ_OUT_E2M1 ? 8u : 10u; }
+inline uint32_t waves_per_cu(int out_dtype, int nb)
+{
+    if (nb == 1)
+        return 12u;
+    return out_dtype == MXQ_OUT_E2M1 ? 8u : 10u;
+}
 
 // When the data rows do not start on 128-byte lines (row pitch F bytes for
 // FP8, F/2 for FP4, not a multiple of 128), neighbouring workgroups share
@@ -92,7 +99,7 @@ int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_
     const int nb = (F % 8 == 0) ? 2 : 1;
     const int64_t nstrips = F / (4 * nb);
     const uint32_t threads = kThreads;
-    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, waves_per_cu(out_dtype));
+    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, waves_per_cu(out_dtype, nb));
     const bool aligned = pitch_aligned(F, out_dtype);
     const int64_t tiles_per_band = (nstrips + threads - 1) / threads;
     const int64_t groups = P / 8;
