@@ -18,6 +18,17 @@
  * Floating point: the pages fix the prescale as an fp32 multiply, so it is
  * done in fp32 here (built without -ffast-math, x86-64 SSE, no FTZ/DAZ).
  * Rounding onto a narrow grid is done exactly in double.
+ *
+ * Parity unpinned: these readings have no page value, worked example or
+ * closed form to be checked against; the code follows the stated reading
+ * and the tests assert that it does:
+ *   - narrow_fp8: a NaN becomes a zero with its sign;
+ *   - mxq_oracle_lane_remap / pack_nibble: stride 2 and parity flag 1;
+ *   - scale_row: the P-row scale image, unplaced rows left untouched;
+ *   - mxq_oracle_prescale: the sign of Inf x (+0) under the alternative
+ *     EMAX with FP4;
+ *   - operand_value (scaled matmul): an E8M0 of 255 makes its elements NaN;
+ *   - mxq_oracle_quantize_axis: the device view of the block axis.
  */
 #include <math.h>
 #include <stdint.h>
