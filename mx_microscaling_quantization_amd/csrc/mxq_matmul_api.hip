@@ -1,6 +1,6 @@
 // mxq_matmul_api.hip -- mxq_scaled_matmul and mxq_scaled_matmul_quantize:
 // operand validation and the launch of scaled_matmul_kernel (one
-// 256-thread workgroup per 256 x 256 output tile) on the caller's stream.
+// 512-thread workgroup per 256 x 256 output tile) on the caller's stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -9,9 +9,11 @@
 // decode(q) * 2^(E8M0 - 127) with the E8M0 of row group k / 32. The kernel
 // computes out[m][n] = sum_k L[k][m] * R[k][n] (K = 4P), fp32 accumulation.
 //
-// Tiling: a 256-thread workgroup computes a 256 x 256 tile of out; each of
-// its 4 waves a 128 x 128 quarter as 4 x 4 MFMAs of 32 x 32 (accumulators in
-// AGPRs). Workgroups are renumbered so that the 32 CUs of one XCD (which
+// Tiling: a 512-thread workgroup computes a 256 x 256 tile of out; each of
+// its 8 waves a 64 (M) x 128 (N) part as 2 x 4 MFMAs of 32 x 32. Two waves
+// share each SIMD and run half a K step apart ("ping-pong"): while one
+// issues its MFMAs, the other reads its next operands from LDS and issues
+// its copies. Workgroups are renumbered so that the 32 CUs of one XCD (which
 // receive every eighth workgroup) work on a compact block of tiles and share
 // operand panels in their L2. Tails in M, N and K read as zeros, so every
 // MFMA runs with all 64 lanes active.
@@ -27,8 +29,7 @@ namespace mxq {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMmTile = 256;        // output tile edge (M and N)
-constexpr int kMmWaveTile = 128;    // per-wave output edge
-constexpr int kMmThreads = 256;
+constexpr int kMmThreads = 512;
 constexpr int kMmXcds = 8;
 constexpr int kMmGroupRows = 4;     // tile rows walked together (L2 reuse)
 constexpr uint32_t kMmBufferFlags = 0x00020000u;   // raw untyped buffer, 32-bit data format
@@ -59,39 +60,45 @@ __device__ __forceinline__ uint32_t mm_bf16_bits(float v)
 // MFMA mapping (measured on gfx950): lane l = i + 32 h supplies row i of A
 // (column i of B); byte b of its 32 pairs with byte b of the same lane half
 // of the other operand; scale block j (one E8M0) is bytes 16 j .. 16 j + 15 of
-// both halves, and half h's scale byte covers block h; result register r of
-// lane l is D[8 (r >> 2) + 4 h + (r & 3)][i].
+// both halves, and half h's scale byte covers block h (op_sel picks the byte
+// of the scale register); result register r of lane l is
+// D[8 (r >> 2) + 4 h + (r & 3)][i].
 // One K step is 64 = 16 operand rows = 4 row quads = 2 row groups (MX
 // blocks). LDS holds each operand row-major, as the copy lands it: row quad
 // q at q * kMmQuadPitch, row 4 q + v of it at + 1024 v, container c at + 4 c.
 // Lane (i, h) supplies rows 4 h .. 4 h + 3 (block 0) and 8 + 4 h .. 11 + 4 h
-// (block 1) of its container: 8 dword reads, VGPR v = row v, on a 256-byte
-// grid so they pair into ds_read2st64_b32. The 128-byte pad of a row quad
-// puts the two lane halves (row quads h and h + 1) in opposite halves of the
-// LDS banks.
+// (block 1) of its container. The containers are interleaved across
+// sub-tiles so that one LDS read serves several: in A sub-tile a (of 2) lane
+// i takes container wm + 2 i + a (one 8-byte read per row feeds both), in B
+// sub-tile u (of 4) container wn + 4 i + u (one 16-byte read per row feeds
+// all four); register moves then gather each sub-tile's 8 dwords. Hence
+// result register r of lane (i, h) in sub-tile (a, u) is
+// out[m0 + wm + 2 (8 (r >> 2) + 4 h + (r & 3)) + a][n0 + wn + 4 i + u]: a lane
+// holds 4 adjacent columns of each row it has, and for each r >> 2 all 8 rows
+// of one 8-row group.
 //
 // In a 64-lane buffer_load_dwordx4 ... lds, lane L's 16 bytes go to LDS base +
 // 16 L: lane L fetches containers 4 L .. 4 L + 3 of one row, and one load
-// copies a 256-container row. Wave w copies row quad w of each operand (8
-// loads) and one scale row (K block w mod 2 of operand w / 2) per step: 9
-// loads. (Dword loads straight into a container-major layout cost four
-// times as many instructions and measured slower than register staging.)
-// kMmStages stages: the copy of step s + kMmStages - 1 is issued during
-// row tiles 0 and 1 of step s into the stage step s - 1 used, and each wave
-// waits for its copy of step s + 1 (the later copies may stay in flight)
-// before the one barrier per step.
+// copies a 256-container row. Wave (g, q) (group g = wave / 4) copies row
+// quad q of operand g (A for g = 0, B for g = 1) per step, 4 loads, and
+// waves with q < 2 one E8M0 row (K block q of the step) of that operand; the
+// other waves issue the same load with an empty range into a spare LDS row,
+// so that every wave has 5 loads per step and one wait count.
+// kMmStages stages: the copies of step s + kMmStages - 1 are issued in a
+// wave's memory phase of step s, into the stage of step s - 1, which every
+// wave has finished reading by then.
 // ----------------------------------------------------------------------------
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kMmSub = kMmWaveTile / 32;                 // 4 x 4 MFMA tiles of 32 x 32 per wave
 constexpr uint32_t kMmStepRows = 16;                      // operand rows per K step (K = 64)
 constexpr int kMmStages = 3;                               // (4 measured no faster)
 constexpr uint32_t kMmQuadPitch = kMmTile * 16 + 128;    // one row quad of a tile, padded
 constexpr uint32_t kMmTileBytes = 4 * kMmQuadPitch;
 constexpr uint32_t kMmScaleBytes = 2 * kMmTile;           // 2 K blocks x 256 containers
 constexpr uint32_t kMmStageBytes = 2 * kMmTileBytes + 2 * kMmScaleBytes;
-constexpr int kMmCopies = 9;                              // loads per wave per step
+constexpr uint32_t kMmSpareBytes = 256;                   // target of the empty scale loads
+constexpr int kMmCopies = 5;                              // loads per wave per step
 
 struct MmSource {
     const uint8_t *data;    // column c0 of operand row 0
@@ -136,111 +143,125 @@ __device__ __forceinline__ void mm_copy_quad(const MmSource &s, uint8_t *tile, u
 }
 
 // E8M0 row of K block kb (256 containers from c0) -> `stile` (LDS); blocks
-// past P / 8 read as zero (their data is zero too).
-__device__ __forceinline__ void mm_copy_scale(const MmSource &s, uint8_t *stile, uint32_t P, uint32_t kb,
-                                               uint32_t dense, uint32_t lane)
+// past P / 8 read as zero (their data is zero too). A wave without a scale
+// row (has == false) loads from an empty range into `spare` instead.
+__device__ __forceinline__ void mm_copy_scale(const MmSource &s, uint8_t *stile, uint8_t *spare, bool has,
+                                               uint32_t P, uint32_t kb, uint32_t dense, uint32_t lane)
 {
-    const bool ok = kb < P / 8;
+    const bool ok = has && kb < P / 8;
     const uint32_t srow = !ok ? 0u : dense ? kb : (kb & 3u) + 32u * (kb >> 2);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(s.scale + (uint64_t)srow * s.C), (short)0, ok ? (int)s.scale_cols : 0, kMmBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)stile, 4, 4u * lane, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(has ? stile : spare), 4, 4u * lane, 0, 0, 0);
 }
 
-// A lane's operand for sub-tile t: its container in rows 4 h + v and
-// 8 + 4 h + v (v = 0..3); `off` = row quad h, container of sub-tile 0.
-__device__ __forceinline__ i32x8_t mm_operand(const uint8_t *tile, uint32_t off, int t)
+// One step's operand bytes of a lane as read from LDS: a[v] = row v's two A
+// containers (v = 0..3: rows 4 h + v; 4..7: rows 8 + 4 h + v - 4), b[v] the
+// four B containers of the same row, and the E8M0 bytes of its K block.
+struct MmRaw {
+    uint32_t a[8][2];
+    uint32_t b[8][4];
+    uint32_t as[2];
+    uint32_t bs;        // byte u: B sub-tile u
+};
+
+// Dword reads (combined into 8- and 16-byte reads by the compiler); typed
+// as 32-bit integers, which lets the compiler see that they do not touch
+// the bytes the buffer-unit copies of the other stages are writing.
+__device__ __forceinline__ void mm_read(const uint8_t *st, uint32_t a_off, uint32_t b_off, uint32_t a_sc,
+                                        uint32_t b_sc, MmRaw &r)
 {
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(tile + off + 128u * t);
-    constexpr uint32_t Q2 = 2 * kMmQuadPitch / 4; // two row quads on, in dwords
-    return i32x8_t{(int)p[0], (int)p[256], (int)p[512], (int)p[768],
-                   (int)p[Q2], (int)p[Q2 + 256], (int)p[Q2 + 512], (int)p[Q2 + 768]};
+#pragma unroll
+    for (int v = 0; v < 8; v++) {
+        const uint32_t roff = (v < 4 ? 0u : 2u * kMmQuadPitch) + 1024u * (v & 3);
+        const uint32_t *pa = reinterpret_cast<const uint32_t *>(st + a_off + roff);
+        const uint32_t *pb = reinterpret_cast<const uint32_t *>(st + b_off + roff);
+        r.a[v][0] = pa[0];
+        r.a[v][1] = pa[1];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            r.b[v][u] = pb[u];
+    }
+    r.as[0] = st[a_sc];
+    r.as[1] = st[a_sc + 1];
+    r.bs = *reinterpret_cast<const uint32_t *>(st + b_sc);
 }
 
 // s_waitcnt encodings (gfx9: vmcnt bits 3..0 and 15..14, expcnt 6..4,
-// lgkmcnt 11..8): the copies of all but the next step may be outstanding,
-// with lgkmcnt(0); and vmcnt(0).
-constexpr int kMmAhead = (kMmStages - 2) * kMmCopies;
+// lgkmcnt 11..8).
+constexpr int mm_wait_vm_lgkm(int vm) { return ((vm >> 4) << 14) | (0x7 << 4) | (vm & 15); }
+constexpr int mm_wait_vm(int vm) { return mm_wait_vm_lgkm(vm) | (0xF << 8); }
+constexpr int kMmAhead = (kMmStages - 2) * kMmCopies;     // loads that may stay in flight
 static_assert(kMmAhead <= 63, "vmcnt counts to 63");
-constexpr int kWaitNextCopyAndLds = ((kMmAhead >> 4) << 14) | (0x7 << 4) | (kMmAhead & 15);
-constexpr int kWaitAllCopies = (0x7 << 4) | (0xF << 8);
+constexpr int kWaitAllCopies = mm_wait_vm(0);
 
-// Quantize-on-produce for the 32 x 32 layout: lane (i, h) holds column
-// 32 b + i, rows 8 k + 4 h .. 8 k + 4 h + 3 (registers 4 k .. 4 k + 3) of sub-tile
-// (a, b). Within each quad of lanes (4 consecutive columns) the bf16 values
-// are transposed so that lane j of the quad holds row 8 k + 4 h + j, columns
-// 4 q .. 4 q + 3: one x4 container. A block (rows 8 k .. 8 k + 7, the quad's
-// columns) is the quad's lanes in both halves; its maximum is a reduction
-// over lanes xor 1, xor 2 and xor 32. Every lane runs the shuffles (full
-// EXEC); only the stores are predicated.
+// Quantize-on-produce: lane (i, h) holds, for each row group k = r >> 2 of
+// its two A sub-tiles, the whole 8 x 4 block at rows m0 + wm + 16 k + 8 h
+// + (2 j + a), j = r & 3, columns n0 + wn + 4 i .. + 3 (B sub-tiles u): the
+// block maximum needs no lane exchange, and each row's 4 values are one x4
+// container.
 template <int OUT>
-__device__ __forceinline__ void mm_quantize_epilogue(const f32x16_t (&acc)[kMmSub][kMmSub], uint32_t row0,
-                                                      uint32_t col0, uint32_t M, uint32_t N, uint32_t lane,
-                                                      uint8_t *__restrict__ data, uint8_t *__restrict__ scale,
-                                                      int emax_bias, uint32_t dense)
+__device__ __forceinline__ void mm_quantize_epilogue(const f32x16_t (&acc)[2][4], uint32_t row0, uint32_t col,
+                                                      uint32_t M, uint32_t N, uint8_t *__restrict__ data,
+                                                      uint8_t *__restrict__ scale, int emax_bias, uint32_t dense)
 {
-    const uint32_t i = lane & 31u, h = lane >> 5, j = lane & 3u, quad = lane & ~3u;
 #pragma unroll
-    for (int a = 0; a < kMmSub; a++)
+    for (int k = 0; k < 4; k++) {
+        const uint32_t row = row0 + 16u * k;   // first row of the block
+        uint32_t w[8][2];
+        uint32_t m2 = 0;
 #pragma unroll
-        for (int b = 0; b < kMmSub; b++)
+        for (int j = 0; j < 4; j++)
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t c01 = mm_bf16_bits(acc[a][b][4 * k]) | mm_bf16_bits(acc[a][b][4 * k + 1]) << 16;
-                const uint32_t c23 = mm_bf16_bits(acc[a][b][4 * k + 2]) | mm_bf16_bits(acc[a][b][4 * k + 3]) << 16;
-                uint32_t hv[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; jj++) {
-                    const uint32_t d01 = (uint32_t)__shfl((int)c01, (int)(quad | jj));
-                    const uint32_t d23 = (uint32_t)__shfl((int)c23, (int)(quad | jj));
-                    hv[jj] = ((j & 2u) ? d23 : d01) >> (16u * (j & 1u)) & 0xFFFFu;
-                }
-                uint32_t w[2] = {hv[0] | hv[1] << 16, hv[2] | hv[3] << 16};
-
-                const uint32_t m2 = pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu);
-                uint32_t mag = max(m2 & 0xFFFFu, m2 >> 16);
-                mag = max(mag, (uint32_t)__shfl_xor((int)mag, 1));
-                mag = max(mag, (uint32_t)__shfl_xor((int)mag, 2));
-                mag = max(mag, (uint32_t)__shfl_xor((int)mag, 32));
-                uint32_t e[1] = {block_e8m0<kInBF16>(mag, emax_bias)};
-                const float sc = e8m0_to_scale(e[0]);
-                const bool special = mag > InfBits<kInBF16>::value || e[0] == 254u;
-
-                const uint32_t row = row0 + 32u * a + 8u * k + 4u * h + j;
-                const uint32_t col = col0 + 32u * b + 4u * (i >> 2);
-                uint32_t out[1];
-                if constexpr (OUT == kOutE2M1)
-                    out[0] = fp4_container<kInBF16, 0>(0u, w[0], w[1], sc);
-                else
-                    out[0] = fp8x4<kInBF16, OUT>(w[0], w[1], sc);
-                if (special)
-                    fix_special_codes<kInBF16, OUT, 1>(w, e, out);
-                if (row < M && col < N) {
-                    if constexpr (OUT == kOutE2M1)
-                        *reinterpret_cast<uint16_t *>(data + ((uint64_t)row * N + col) / 2) = (uint16_t)out[0];
-                    else
-                        *reinterpret_cast<uint32_t *>(data + (uint64_t)row * N + col) = out[0];
-                    if (j == 0 && h == 0) { // the block's first row writes its E8M0
-                        const uint32_t grp = row / 8;
-                        const uint64_t slot = dense ? grp : (grp & 3u) + 32ull * (grp >> 2);
-                        scale[slot * (N / 4) + col / 4] = (uint8_t)e[0];
-                    }
-                }
+            for (int a = 0; a < 2; a++) {
+                const int r = 4 * k + j;
+                uint32_t *x = w[2 * j + a];
+                x[0] = mm_bf16_bits(acc[a][0][r]) | mm_bf16_bits(acc[a][1][r]) << 16;
+                x[1] = mm_bf16_bits(acc[a][2][r]) | mm_bf16_bits(acc[a][3][r]) << 16;
+                m2 = pk_max_u16(m2, pk_max_u16(x[0] & 0x7FFF7FFFu, x[1] & 0x7FFF7FFFu));
             }
+        const uint32_t mag = max(m2 & 0xFFFFu, m2 >> 16);
+        uint32_t e[1] = {block_e8m0<kInBF16>(mag, emax_bias)};
+        const float sc = e8m0_to_scale(e[0]);
+        const bool special = mag > InfBits<kInBF16>::value || e[0] == 254u;
+        if (row >= M || col >= N)
+            continue;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            uint32_t out[1];
+            if constexpr (OUT == kOutE2M1)
+                out[0] = fp4_container<kInBF16, 0>(0u, w[t][0], w[t][1], sc);
+            else
+                out[0] = fp8x4<kInBF16, OUT>(w[t][0], w[t][1], sc);
+            if (special)
+                fix_special_codes<kInBF16, OUT, 1>(w[t], e, out);
+            const uint64_t o = (uint64_t)(row + t) * N + col;
+            if constexpr (OUT == kOutE2M1)
+                *reinterpret_cast<uint16_t *>(data + o / 2) = (uint16_t)out[0];
+            else
+                *reinterpret_cast<uint32_t *>(data + o) = out[0];
+        }
+        const uint32_t grp = row / 8;
+        const uint64_t slot = dense ? grp : (grp & 3u) + 32ull * (grp >> 2);
+        scale[slot * (N / 4) + col / 4] = (uint8_t)e[0];
+    }
 }
 
+// M and N are multiples of 4 (checked on the host), so a row's 4 adjacent
+// results are one aligned 16-byte (f32) or 8-byte (bf16) store.
 template <int FMT, int EPI>
 __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
     const uint8_t *__restrict__ lhs, const uint8_t *__restrict__ lhs_scale, const uint8_t *__restrict__ rhs,
     const uint8_t *__restrict__ rhs_scale, uint32_t P, uint32_t M, uint32_t N, uint32_t tiles_n, uint32_t dense,
     void *__restrict__ out, uint8_t *__restrict__ out_scale, int emax_bias)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMmStages * kMmStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMmStages * kMmStageBytes + kMmSpareBytes];
     constexpr int F = MfmaFmt<FMT>::value;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t grp = wave >> 2, wq = wave & 3u;
     const uint32_t i = lane & 31u, h = lane >> 5;
 
     // Tile order. Workgroup w runs on XCD w % 8, so XCD x is given the
@@ -260,139 +281,118 @@ __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
     const uint32_t in_group = t - group * kMmGroupRows * tiles_n;
     const uint32_t m0 = (first_row + in_group % rows_in_group) * kMmTile;
     const uint32_t n0 = (in_group / rows_in_group) * kMmTile;
-    const uint32_t wm = (wave >> 1) * kMmWaveTile, wn = (wave & 1u) * kMmWaveTile;
+    const uint32_t wm = 64u * wq, wn = 128u * grp;
     const uint32_t nsteps = (P + kMmStepRows - 1) / kMmStepRows;
 
-    MmSource src_a, src_b;
-    mm_source(src_a, lhs, lhs_scale, M, m0);
-    mm_source(src_b, rhs, rhs_scale, N, n0);
-    MmSource src_s;                                        // this wave's scale rows
-    mm_source(src_s, wave < 2 ? lhs : rhs, wave < 2 ? lhs_scale : rhs_scale, wave < 2 ? M : N, wave < 2 ? m0 : n0);
-    const uint32_t s_kb = wave & 1u, s_off = (wave < 2 ? 0u : kMmScaleBytes) + kMmTile * s_kb;
+    MmSource src;                                          // the operand this wave copies
+    mm_source(src, grp ? rhs : lhs, grp ? rhs_scale : lhs_scale, grp ? N : M, grp ? n0 : m0);
+    const uint32_t t_off = grp ? kMmTileBytes : 0u;
+    const bool has_scale = wq < 2u;
+    const uint32_t s_off = 2u * kMmTileBytes + (grp ? kMmScaleBytes : 0u) + kMmTile * (wq & 1u);
+    uint8_t *spare = lds + kMmStages * kMmStageBytes;
 
-    // lane-constant LDS offsets of the operand reads (sub-tile 0)
-    const uint32_t a_off = kMmQuadPitch * h + 4u * (wm + i);
-    const uint32_t b_off = kMmTileBytes + kMmQuadPitch * h + 4u * (wn + i);
-    const uint32_t a_sc = 2 * kMmTileBytes + kMmTile * h + wm + i;
-    const uint32_t b_sc = 2 * kMmTileBytes + kMmScaleBytes + kMmTile * h + wn + i;
+    // lane-constant LDS offsets of the operand reads
+    const uint32_t a_off = kMmQuadPitch * h + 4u * (wm + 2u * i);
+    const uint32_t b_off = kMmTileBytes + kMmQuadPitch * h + 4u * (wn + 4u * i);
+    const uint32_t a_sc = 2u * kMmTileBytes + kMmTile * h + wm + 2u * i;
+    const uint32_t b_sc = 2u * kMmTileBytes + kMmScaleBytes + kMmTile * h + wn + 4u * i;
 
-    f32x16_t acc[kMmSub][kMmSub];
+    f32x16_t acc[2][4];
 #pragma unroll
-    for (int a = 0; a < kMmSub; a++)
+    for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int b = 0; b < kMmSub; b++)
-            acc[a][b] = f32x16_t{};
+        for (int u = 0; u < 4; u++)
+            acc[a][u] = f32x16_t{};
 
     // prologue: steps 0 .. kMmStages - 2 into stages 0 .. kMmStages - 2
 #pragma unroll
     for (uint32_t st = 0; st < kMmStages - 1; st++) {
         uint8_t *stage = lds + st * kMmStageBytes;
-        mm_copy_quad(src_a, stage, P, st, wave, lane);
-        mm_copy_quad(src_b, stage + kMmTileBytes, P, st, wave, lane);
-        mm_copy_scale(src_s, stage + 2 * kMmTileBytes + s_off, P, 2 * st + s_kb, dense, lane);
+        mm_copy_quad(src, stage + t_off, P, st, wq, lane);
+        mm_copy_scale(src, stage + s_off, spare, has_scale, P, 2 * st + (wq & 1u), dense, lane);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitNextCopyAndLds);
+    __builtin_amdgcn_s_waitcnt(mm_wait_vm(kMmAhead));     // step 0 has landed
     __builtin_amdgcn_s_barrier();
+    // Group 1 runs half a step behind: barrier j closes group 0's memory
+    // phase and group 1's compute phase (j even), or the other way round.
+    // Every wave passes 2 nsteps + 2 barriers.
+    if (grp)
+        __builtin_amdgcn_s_barrier();
 
-    i32x8_t bop[kMmSub];
-    int bsc[kMmSub];
-    i32x8_t aop = mm_operand(lds, a_off, 0);
-    int asc = lds[a_sc];
-#pragma unroll
-    for (int b = 0; b < kMmSub; b++) {
-        bop[b] = mm_operand(lds, b_off, b);
-        bsc[b] = lds[b_sc + 32u * b];
-    }
-
-    // Per step s (stage s mod kMmStages): row tile a issues its 4 MFMAs and
-    // reads the next row tile's A operand; row tiles 0 and 1 also issue the
-    // copy of step s + kMmStages - 1 into step s - 1's stage, free since the
-    // previous barrier; before row tile 3 every wave waits for its copy of
-    // step s + 1 and for its LDS reads, then one barrier; row tile 3 reads
-    // step s + 1's B operands and first A operand between its MFMAs.
     uint32_t cur_i = 0;
     for (uint32_t s = 0; s < nsteps; s++) {
-        const uint32_t nxt_i = cur_i == kMmStages - 1 ? 0u : cur_i + 1u;
-        const uint32_t fre_i = cur_i == 0 ? kMmStages - 1 : cur_i - 1u; // step s - 1's stage
+        const uint32_t fre_i = cur_i == 0 ? kMmStages - 1 : cur_i - 1u;   // step s - 1's stage
         const uint8_t *cur = lds + cur_i * kMmStageBytes;
-        const uint8_t *nxt = lds + nxt_i * kMmStageBytes;
         uint8_t *fre = lds + fre_i * kMmStageBytes;
+
+        // memory phase: read step s's operands, copy step s + kMmStages - 1;
+        // then wait for my reads and for my copies of step s + 1 (the barrier
+        // then makes everyone's copies of step s + 1 visible)
+        __builtin_amdgcn_sched_barrier(0);
+        MmRaw r;
+        mm_read(cur, a_off, b_off, a_sc, b_sc, r);
+        const uint32_t ahead = s + kMmStages - 1;
+        mm_copy_quad(src, fre + t_off, P, ahead, wq, lane);
+        mm_copy_scale(src, fre + s_off, spare, has_scale, P, 2 * ahead + (wq & 1u), dense, lane);
+        __builtin_amdgcn_s_waitcnt(mm_wait_vm_lgkm(kMmAhead));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+
+        // compute phase: gather the sub-tile operands, 8 MFMAs
+        i32x8_t aop[2], bop[4];
 #pragma unroll
-        for (int a = 0; a < kMmSub; a++) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (a == kMmSub - 1) {
-                __builtin_amdgcn_s_waitcnt(kWaitNextCopyAndLds);
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            i32x8_t an;
-            int ans;
-            if (a + 1 < kMmSub) {
-                an = mm_operand(cur, a_off, a + 1);
-                ans = cur[a_sc + 32u * (a + 1)];
-            } else {
-                an = mm_operand(nxt, a_off, 0);
-                ans = nxt[a_sc];
-            }
-            const uint32_t ahead = s + kMmStages - 1;
-            if (a == 0) {
-                mm_copy_quad(src_a, fre, P, ahead, wave, lane);
-                mm_copy_scale(src_s, fre + 2 * kMmTileBytes + s_off, P, 2 * ahead + s_kb, dense, lane);
-            }
-            if (a == 1)
-                mm_copy_quad(src_b, fre + kMmTileBytes, P, ahead, wave, lane);
+        for (int a = 0; a < 2; a++)
+            aop[a] = i32x8_t{(int)r.a[0][a], (int)r.a[1][a], (int)r.a[2][a], (int)r.a[3][a],
+                             (int)r.a[4][a], (int)r.a[5][a], (int)r.a[6][a], (int)r.a[7][a]};
 #pragma unroll
-            for (int b = 0; b < kMmSub; b++) {
-                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[b], acc[a][b], F, F, 0, asc, 0,
-                                                                            bsc[b]);
-                if (a == kMmSub - 1) {
-                    bop[b] = mm_operand(nxt, b_off, b);
-                    bsc[b] = nxt[b_sc + 32u * b];
-                }
-            }
-            // instruction order inside the row tile (masks: 0x008 MFMA,
-            // 0x100 LDS read, 0x020 global load)
-            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);          // next A operand first
+        for (int u = 0; u < 4; u++)
+            bop[u] = i32x8_t{(int)r.b[0][u], (int)r.b[1][u], (int)r.b[2][u], (int)r.b[3][u],
+                             (int)r.b[4][u], (int)r.b[5][u], (int)r.b[6][u], (int)r.b[7][u]};
 #pragma unroll
-            for (int b = 0; b < kMmSub; b++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (a == kMmSub - 1)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // next step's B operand b
-                else if (a == 0 && b == 0)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-                else if (a <= 1)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
-            aop = an;
-            asc = ans;
+        for (int a = 0; a < 2; a++) {
+            acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[a], bop[0], acc[a][0], F, F, 0,
+                                                                        (int)r.as[a], 0, (int)r.bs);
+            acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[a], bop[1], acc[a][1], F, F, 0,
+                                                                        (int)r.as[a], 1, (int)r.bs);
+            acc[a][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[a], bop[2], acc[a][2], F, F, 0,
+                                                                        (int)r.as[a], 2, (int)r.bs);
+            acc[a][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[a], bop[3], acc[a][3], F, F, 0,
+                                                                        (int)r.as[a], 3, (int)r.bs);
         }
-        cur_i = nxt_i;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        cur_i = cur_i == kMmStages - 1 ? 0u : cur_i + 1u;
     }
+    if (!grp)
+        __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_waitcnt(kWaitAllCopies);
 
+    const uint32_t col = n0 + wn + 4u * i;
+    const uint32_t row0 = m0 + wm + 8u * h;   // + 16 (r >> 2) + 2 (r & 3) + a
     if constexpr (EPI >= kEpiMx) {
-        mm_quantize_epilogue<EPI - kEpiMx>(acc, m0 + wm, n0 + wn, M, N, lane, reinterpret_cast<uint8_t *>(out),
-                                            out_scale, emax_bias, dense);
+        mm_quantize_epilogue<EPI - kEpiMx>(acc, row0, col, M, N, reinterpret_cast<uint8_t *>(out), out_scale,
+                                            emax_bias, dense);
         return;
     }
-    // result register r of lane (i, h) in sub-tile (a, b) is
-    // out[m0 + wm + 32a + 8(r >> 2) + 4h + (r & 3)][n0 + wn + 32b + i]
+    if (col >= N)
+        return;
 #pragma unroll
-    for (int a = 0; a < kMmSub; a++)
+    for (int r = 0; r < 16; r++)
 #pragma unroll
-        for (int b = 0; b < kMmSub; b++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const uint32_t m = m0 + wm + 32u * a + 8u * (r >> 2) + 4u * h + (r & 3);
-                const uint32_t n = n0 + wn + 32u * b + i;
-                if (m < M && n < N) {
-                    const uint64_t o = (uint64_t)m * N + n;
-                    if constexpr (EPI == kEpiF32)
-                        reinterpret_cast<float *>(out)[o] = acc[a][b][r];
-                    else
-                        reinterpret_cast<uint16_t *>(out)[o] = (uint16_t)mm_bf16_bits(acc[a][b][r]);
-                }
-            }
+        for (int a = 0; a < 2; a++) {
+            const uint32_t m = row0 + 16u * (r >> 2) + 2u * (r & 3) + a;
+            if (m >= M)
+                continue;
+            const uint64_t o = (uint64_t)m * N + col;
+            if constexpr (EPI == kEpiF32)
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + o) =
+                    float4{acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]};
+            else
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + o) =
+                    uint2{mm_bf16_bits(acc[a][0][r]) | mm_bf16_bits(acc[a][1][r]) << 16,
+                          mm_bf16_bits(acc[a][2][r]) | mm_bf16_bits(acc[a][3][r]) << 16};
+        }
 }
 
 } // namespace mxq
