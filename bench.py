@@ -37,6 +37,11 @@ per step as the quantize).
 in the kernel's epilogue (format ``--out``, default e4m3fn), and reports the
 unfused pair (bf16 matmul, then quantize) on the same operands beside it.
 
+The matmul ops warm up with 200 untimed launches by default (the streaming
+ops with 5): under sustained FP8 MFMA work the GPU clock first drops below
+its steady value and takes some 30 ms of load to settle, so a short
+warm-up would time that transient rather than the sustained rate.
+
 With the CPU baseline on (the default), the quantize line carries two
 figures for the oracle on the same input: ``cpu_baseline`` (one thread on
 leading row slabs, about 12 s of oracle time) and ``cpu_baseline_all_cores``
@@ -283,6 +288,9 @@ def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block:
                       % (done, block, block, 4 * P, spent)}
 
 
+MATMUL_WARMUP = 200
+
+
 def _time_steps(step, steps: int, warmup: int, stream, pre=None):
     """Time `steps` calls of `step` on `stream` after `warmup` untimed ones.
 
@@ -414,7 +422,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default 5; 200 for the matmul ops)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--out", default=None, help="output format (default: the workload's first)")
     ap.add_argument("--op", choices=("quantize", "dequantize", "matmul", "matmul_quantize", "quantize_axis"),
@@ -425,7 +434,7 @@ def main() -> int:
                     help="matmul sizes (M, N multiples of 4, K a multiple of 32)")
     ap.add_argument("--res", choices=("bf16", "f32"), default="bf16", help="dequantize result type")
     ap.add_argument("--cache", choices=("hot", "flushed"), default="hot",
-                    help="flushed: write 512 MiB between launches and time the launches alone")
+                    help="flushed: read 512 MiB between launches and time the launches alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -434,6 +443,8 @@ def main() -> int:
         print("bench.py: this path runs on one GPU only; --gpus %d is not supported "
               "(rows shard with no exchange, see the design notes)" % args.gpus, file=sys.stderr)
         return 2
+    if args.warmup is None:
+        args.warmup = MATMUL_WARMUP if args.op in ("matmul", "matmul_quantize") else 5
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
