@@ -96,6 +96,15 @@ def test_matmul_against_oracle(P, M, N, fmt, res):
     check(P, M, N, fmt, res, seed=P + M + N)
 
 
+@pytest.mark.parametrize("fmt,res", [("e4m3fn", torch.float32), ("e5m2", torch.bfloat16)])
+def test_matmul_many_tiles(fmt, res):
+    """5 x 5 output tiles (both edges ragged) and a K tail: the per-XCD tile
+    ranges (24 tiles, 3 per XCD, and one tile past them), a short last
+    group of tile rows, and a half-filled last K step."""
+    progress("matmul %s %s P=24 M=1100 N=1160" % (fmt, res))
+    check(24, 1100, 1160, fmt, res, seed=17)
+
+
 @pytest.mark.parametrize("P,M,N", [(64, 132, 68), (256, 256, 128)])
 def test_matmul_dense_scales(P, M, N):
     check(P, M, N, "e4m3fn", torch.float32, dense=True, seed=3)
