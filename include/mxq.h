@@ -228,7 +228,8 @@ size_t mxq_result_bytes(int64_t P, int64_t F, int res_dtype);
  *                   zero result (the operand pointers may then be NULL).
  *   M, N            multiples of 4; M == 0 or N == 0 is an empty call.
  *                   M, N <= MXQ_MATMUL_MAX_COLS, else MXQ_E_OVERFLOW (the
- *                   kernel addresses 32 operand rows with 32-bit offsets).
+ *                   kernel addresses one K step, 16 operand rows of 4M or
+ *                   4N bytes, with 32-bit offsets: 64 * 2^25 = 2^31).
  *   fmt             MXQ_OUT_E4M3FN or MXQ_OUT_E5M2 (both operands).
  *   res_dtype       MXQ_RES_F32 or MXQ_RES_BF16 (the fp32 sum rounded to
  *                   nearest-even).
