@@ -149,7 +149,9 @@ __device__ __forceinline__ void mm_copy_scale(const MmSource &s, uint8_t *stile,
                                                uint32_t P, uint32_t kb, uint32_t dense, uint32_t lane)
 {
     const bool ok = has && kb < P / 8;
-    const uint32_t srow = !ok ? 0u : dense ? kb : (kb & 3u) + 32u * (kb >> 2);
+    // uniform; said so, or the compiler builds the address in vector
+    // registers and loops over its (single) value
+    const uint32_t srow = __builtin_amdgcn_readfirstlane(!ok ? 0u : dense ? kb : (kb & 3u) + 32u * (kb >> 2));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(s.scale + (uint64_t)srow * s.C), (short)0, ok ? (int)s.scale_cols : 0, kMmBufferFlags);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(has ? stile : spare), 4, 4u * lane, 0, 0, 0);
@@ -165,9 +167,12 @@ struct MmRaw {
     uint32_t bs;        // byte u: B sub-tile u
 };
 
-// Dword reads (combined into 8- and 16-byte reads by the compiler); typed
-// as 32-bit integers, which lets the compiler see that they do not touch
-// the bytes the buffer-unit copies of the other stages are writing.
+// Dword reads, which the compiler combines into 8- and 16-byte reads. Read
+// through a 16-byte vector type instead, they got a wait for every copy in
+// flight (vmcnt(0)) in front of them; read as 32-bit integers they do not.
+// No such wait is needed: the reads' stage was completed by the wait and
+// barrier that closed the previous phase, and the copies in flight write
+// other stages.
 __device__ __forceinline__ void mm_read(const uint8_t *st, uint32_t a_off, uint32_t b_off, uint32_t a_sc,
                                         uint32_t b_sc, MmRaw &r)
 {
