@@ -291,6 +291,15 @@ def cpu_baseline_matmul(dl, sl, dr, sr, fmt: str, budget_s: float = 10.0, block:
 MATMUL_WARMUP = 200
 
 
+def default_warmup(op: str, warmup: int | None) -> int:
+    """The warm-up to use: the one given, else 200 launches for the matmul
+    ops (whose clock takes that long to settle under FP8 MFMA load) and 5
+    for the streaming ops."""
+    if warmup is not None:
+        return warmup
+    return MATMUL_WARMUP if op in ("matmul", "matmul_quantize") else 5
+
+
 def _time_steps(step, steps: int, warmup: int, stream, pre=None):
     """Time `steps` calls of `step` on `stream` after `warmup` untimed ones.
 
@@ -443,8 +452,7 @@ def main() -> int:
         print("bench.py: this path runs on one GPU only; --gpus %d is not supported "
               "(rows shard with no exchange, see the design notes)" % args.gpus, file=sys.stderr)
         return 2
-    if args.warmup is None:
-        args.warmup = MATMUL_WARMUP if args.op in ("matmul", "matmul_quantize") else 5
+    args.warmup = default_warmup(args.op, args.warmup)
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2

@@ -98,6 +98,15 @@ def test_no_gpu_fails_loudly():
     assert r.stdout == ""
 
 
+def test_default_warmup():
+    assert bench.default_warmup("quantize", None) == 5
+    assert bench.default_warmup("dequantize", None) == 5
+    assert bench.default_warmup("quantize_axis", None) == 5
+    assert bench.default_warmup("matmul", None) == bench.MATMUL_WARMUP == 200
+    assert bench.default_warmup("matmul_quantize", None) == 200
+    assert bench.default_warmup("matmul", 3) == 3 and bench.default_warmup("quantize", 0) == 0
+
+
 def test_host_cpu_record():
     h = bench.host_cpu()
     assert isinstance(h["model"], str) and h["model"]
