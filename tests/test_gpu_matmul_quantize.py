@@ -127,6 +127,15 @@ def test_matmul_quantize_against_oracle(P, M, N, fmt, out_dtype):
     run_case(P, M, N, fmt, out_dtype, seed=P + M + N)
 
 
+@pytest.mark.parametrize("out_dtype", ["e4m3fn", "e5m2", "e2m1"])
+def test_matmul_quantize_many_tiles(out_dtype):
+    """5 x 5 output tiles, both edges ragged, a K tail, and 138 row groups (scale
+    image rows up to 1089): fused bytes equal the unfused pair's, whose two
+    kernels the oracle checks separately."""
+    progress("matmul_quantize e4m3fn -> %s P=24 M=1104 N=1160" % out_dtype)
+    run_case(24, 1104, 1160, "e4m3fn", out_dtype, seed=23, oracle_check=False)
+
+
 @pytest.mark.parametrize("out_dtype", ["e4m3fn", "e2m1"])
 @pytest.mark.parametrize("alt,dense", [(True, False), (False, True), (True, True)])
 def test_matmul_quantize_modes(out_dtype, alt, dense):
