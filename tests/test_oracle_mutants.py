@@ -54,6 +54,15 @@ MUTANTS = [
     ("axis view reverses each container", "                int64_t k = 4 * p + j;",
      "                int64_t k = 4 * p + (3 - j);"),
     ("bf16 rounding ties away from even", "(dropped == 0x8000u && (keep & 1u))", "(dropped == 0x8000u)"),
+    ("FP4 decode of 0.5 as 0.25", "v = m ? 0.5 : 0.0;", "v = m ? 0.25 : 0.0;"),
+    ("FP8 subnormals one binade low", "v = ldexp((double)m, 1 - bias - mbits);",
+     "v = ldexp((double)m, -bias - mbits);"),
+    ("e4m3fn NaN at 0x7E", "ef == 15 && m == 7)", "ef == 15 && m == 6)"),
+    ("axis dim -2 mirrors the other axis", "in[k * C + o];", "in[k * C + (O - 1 - o)];"),
+    ("fused result truncated to bf16", "res[k] = mxq_oracle_f32_to_bf16((float)sum[k]);",
+     "res[k] = (uint16_t)(bits_of((float)sum[k]) >> 16);"),
+    ("dense layout uses the image slot", "return layout == ORC_SCALE_DENSE ? i : mxq_oracle_scale_slot(i);",
+     "return mxq_oracle_scale_slot(i);"),
 ]
 
 
