@@ -27,7 +27,8 @@
  *   - scale_row: the P-row scale image, unplaced rows left untouched;
  *   - mxq_oracle_prescale: the sign of Inf x (+0) under the alternative
  *     EMAX with FP4;
- *   - operand_value (scaled matmul): an E8M0 of 255 makes its elements NaN;
+ *   - operand_value (scaled matmul) and mxq_oracle_dequantize: an E8M0 of
+ *     255 is the scale 2^128, like every other byte 2^(E8M0 - 127);
  *   - mxq_oracle_quantize_axis: the device view of the block axis.
  */
 #include <math.h>
@@ -108,16 +109,18 @@ int mxq_oracle_emax(int out_dtype)
  * ---------------------------------------------------------------------- */
 uint8_t mxq_oracle_block_max_exponent(const float *x, int64_t F, int64_t row_group, int64_t col_block)
 {
-    uint8_t exps[32];
-    int n = 0;
-    for (int64_t r = 8 * row_group; r < 8 * row_group + 8; r++)
-        for (int64_t c = 4 * col_block; c < 4 * col_block + 4; c++)
-            exps[n++] = (uint8_t)(bits_of(x[r * F + c]) >> 23);
-    uint8_t m = exps[0];
-    for (int k = 1; k < 32; k++)
-        if (exps[k] > m)
-            m = exps[k];
-    return m;
+    unsigned largest = 0;
+    for (int64_t dr = 0; dr < 8; dr++) {
+        const float *row = x + (8 * row_group + dr) * F + 4 * col_block;
+        for (int64_t dc = 0; dc < 4; dc++) {
+            /* bits 23..30 of an fp32 are its biased exponent field; the
+             * sign (bit 31) is not part of it */
+            unsigned field = (bits_of(row[dc]) >> 23) & 0xFFu;
+            if (field > largest)
+                largest = field;
+        }
+    }
+    return (uint8_t)largest;
 }
 
 /* ------------------------------------------------------------------------
@@ -126,15 +129,14 @@ uint8_t mxq_oracle_block_max_exponent(const float *x, int64_t F, int64_t row_gro
  * from the block's maximum exponent, floor a negative result at 0, then
  * raise a 0 byte to 1. The result is never 0.
  * ---------------------------------------------------------------------- */
+static int int_max(int a, int b) { return a > b ? a : b; }
+
 uint8_t mxq_oracle_e8m0(uint8_t max_exponent, int emax_bias)
 {
-    int v = (int)max_exponent - emax_bias;
-    if (v < 0)
-        v = 0;            /* no down-scaling below unity */
-    uint8_t byte = (uint8_t)v;
-    if (byte == 0)
-        byte = 1;         /* all-zero / all-tiny block keeps 2^-126 */
-    return byte;
+    /* max(1, max(0, m - bias)): the inner bound keeps the unsigned byte
+     * from going negative, the outer one then lifts a 0 byte (2^-127) to 1
+     * (2^-126) */
+    return (uint8_t)int_max(1, int_max(0, (int)max_exponent - emax_bias));
 }
 
 /* ------------------------------------------------------------------------
@@ -300,37 +302,42 @@ double mxq_oracle_decode(uint8_t code, int out_dtype)
 /* ------------------------------------------------------------------------
  * Step 6 -- FP4 container lane order.
  * [NUM] "x4-Pack and Scale-Tensor Interleave", FP4 x4-Pack and Intra-x4
- * Lane Order: within each window of 2*stride nibble indices the index is
- * mirrored, and an even index is then moved back by two; the remapped index
- * r picks byte r/2, and the nibble goes high when r's low bit equals the
- * parity flag.
+ * Lane Order: the nibble index is permuted inside windows of 2 * stride
+ * nibbles before it picks a byte (index / 2) and a half of that byte (the
+ * high half when the index's low bit equals the parity flag). The page's
+ * window formula amounts to reversing the byte order inside each window
+ * (worked out below; tests/golden/fp4_container_order.txt holds the table
+ * for stride 2).
  * reading: stride 2 (one window = the four nibbles of one x4 container) and
  * parity flag 1 (an odd remapped index is the high nibble); the page leaves
  * both to an unrecovered access-pattern rule.
  * ---------------------------------------------------------------------- */
 int64_t mxq_oracle_lane_remap(int64_t index, int64_t stride)
 {
-    int64_t w = 2 * stride;
-    int64_t window = index / w;
-    int64_t pos = index % w;
-    int64_t r = w * (window + 1) - pos;
-    if ((index & 1) == 0)
-        r -= 2;
-    return r;
+    /* Worked out from the page's formula: nibble index 2 * b + t (byte b,
+     * t = 0 low / 1 high in the naive order) keeps t and moves to byte
+     * stride - 1 - b' of its window of `stride` bytes (b' = b mod stride):
+     * the byte order inside each window is reversed. Stride 1 changes
+     * nothing, and applying the map twice gives the index back. */
+    int64_t t = index & 1;
+    int64_t b = index >> 1;
+    int64_t first = b - b % stride;
+    int64_t mirrored = first + (stride - 1 - b % stride);
+    return 2 * mirrored + t;
 }
 
 #define ORC_FP4_STRIDE 2
 #define ORC_FP4_PARITY 1
 
+/* Put the 4-bit code of element `index` (row-major over the tensor) into the
+ * packed data: byte r / 2 of the remapped index r, in the high half when
+ * r's low bit equals the parity flag. */
 static void pack_nibble(uint8_t *base, int64_t index, uint8_t nibble)
 {
     int64_t r = mxq_oracle_lane_remap(index, ORC_FP4_STRIDE);
-    uint8_t *dst = base + (r >> 1);
-    uint8_t nib = nibble & 0xF;
-    if ((r & 1) == ORC_FP4_PARITY)
-        *dst = (uint8_t)((*dst & 0x0F) | (nib << 4));
-    else
-        *dst = (uint8_t)((*dst & 0xF0) | nib);
+    unsigned shift = (r & 1) == ORC_FP4_PARITY ? 4u : 0u;
+    unsigned kept = base[r / 2] & ~(0xFu << shift);
+    base[r / 2] = (uint8_t)(kept | ((nibble & 0xFu) << shift));
 }
 
 /* ------------------------------------------------------------------------
@@ -563,9 +570,12 @@ int mxq_oracle_dequantize(const uint8_t *data, const uint8_t *scale_image, int64
  * X[k][c] = decode(data[p][4c + j]) * 2^(S[k / 32][c] - 127), where S is the
  * logical scale (row k/32 = row group p/8). The result is
  * out[m][n] = sum_k L[k][m] * R[k][n], formed here in double.
- * reading: an E8M0 byte of 255 makes its 32 elements NaN here (the OCP MX
- * meaning of 0xFF); the quantizer never writes it, and the pages' own
- * dequantize (ldexpf) is kept unchanged by mxq_oracle_dequantize.
+ * reading: every E8M0 byte e, 255 included, is the scale 2^(e - 127): the
+ * numerics page gives the consumer's dequant as ldexpf(x, E8M0 - 127) and
+ * no exception for any byte. This is the element value mxq_oracle_dequantize
+ * rounds to its result type; here it enters the sum exactly (the double
+ * range holds every such product), so the two consumers agree on what each
+ * element is worth.
  * lhs: P x 4M bytes, rhs: P x 4N bytes; scales as images (or dense arrays).
  * out: M x N doubles, row-major.
  * ---------------------------------------------------------------------- */
@@ -575,8 +585,6 @@ static double operand_value(const uint8_t *data, const uint8_t *scale, int64_t C
     int64_t p = k / 4, j = k % 4;
     double v = mxq_oracle_decode(data[p * 4 * C + 4 * c + j], fmt);
     int e = scale[scale_row(k / 32, scale_layout) * C + c];
-    if (e == 255)
-        return NAN;
     return ldexp(v, e - 127);
 }
 

@@ -23,13 +23,13 @@ FAST = "not exhaustive and not dense_fp32_range"
 MUTANTS = [
     ("emax e4m3fn 8 -> 7", "case ORC_OUT_E4M3FN: return 8;", "case ORC_OUT_E4M3FN: return 7;"),
     ("emax e2m1 2 -> 3", "case ORC_OUT_E2M1: return 2;", "case ORC_OUT_E2M1: return 3;"),
-    ("e8m0 zero not raised to 1", "byte = 1;         /* all-zero", "byte = 0;         /* all-zero"),
-    ("e8m0 negative mirrored, not floored", "        v = 0;            /* no down-scaling",
-     "        v = -v;           /* no down-scaling"),
-    ("block exponent byte shifted by 24", "(uint8_t)(bits_of(x[r * F + c]) >> 23)",
-     "(uint8_t)(bits_of(x[r * F + c]) >> 24)"),
-    ("block drops its last row", "r < 8 * row_group + 8; r++)", "r < 8 * row_group + 7; r++)"),
-    ("block drops its last column", "c < 4 * col_block + 4; c++)", "c < 4 * col_block + 3; c++)"),
+    ("e8m0 zero not raised to 1", "int_max(1, int_max(0,", "int_max(0, int_max(0,"),
+    ("e8m0 negative mirrored, not floored", "int_max(0, (int)max_exponent - emax_bias)",
+     "abs((int)max_exponent - emax_bias)"),
+    ("block exponent byte shifted by 24", "(bits_of(row[dc]) >> 23) & 0xFFu",
+     "(bits_of(row[dc]) >> 24) & 0xFFu"),
+    ("block drops its last row", "dr < 8; dr++)", "dr < 7; dr++)"),
+    ("block drops its last column", "dc < 4; dc++)", "dc < 3; dc++)"),
     ("prescale exponent field 253 - e", "(254 - (int)e8m0)", "(253 - (int)e8m0)"),
     ("ties round up, not to even", "(rest == 0.5 && fmod(n, 2.0) != 0.0)", "(rest == 0.5)"),
     ("e4m3fn largest code 0x7D", "narrow_fp8(y, 3, -6, 448.0, 0x7E)", "narrow_fp8(y, 3, -6, 448.0, 0x7D)"),
@@ -39,7 +39,9 @@ MUTANTS = [
      "(b >> 31) << 7);\n    if (isnan(y))\n        return 0;"),
     ("FP4 NaN loses its sign", "(b >> 31) << 3);\n    if (isnan(y))\n        return sign;",
      "(b >> 31) << 3);\n    if (isnan(y))\n        return 0;"),
-    ("lane remap without the even shift", "        r -= 2;", "        r -= 0;"),
+    ("lane remap without the byte mirror", "first + (stride - 1 - b % stride);", "first + b % stride;"),
+    ("lane remap mirrors across the whole window of nibbles", "return 2 * mirrored + t;",
+     "return 2 * mirrored + (1 - t);"),
     ("FP4 nibble parity 0", "#define ORC_FP4_PARITY 1", "#define ORC_FP4_PARITY 0"),
     ("scale slot stride 16", "(i & 3) + 32 * (i >> 2)", "(i & 3) + 16 * (i >> 2)"),
     ("f16 subnormal step 2^-25", "mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
@@ -51,6 +53,7 @@ MUTANTS = [
     ("dequantize scale 2^(e - 126)", "(float)ldexp(v, (int)srow[f / 4] - 127)", "(float)ldexp(v, (int)srow[f / 4] - 126)"),
     ("matmul reads a container backwards", "int64_t p = k / 4, j = k % 4;", "int64_t p = k / 4, j = 3 - k % 4;"),
     ("matmul scale 2^(e - 128)", "    return ldexp(v, e - 127);", "    return ldexp(v, e - 128);"),
+    ("matmul reads E8M0 255 as NaN", "    return ldexp(v, e - 127);", "    return e == 255 ? NAN : ldexp(v, e - 127);"),
     ("axis view reverses each container", "                int64_t k = 4 * p + j;",
      "                int64_t k = 4 * p + (3 - j);"),
     ("bf16 rounding ties away from even", "(dropped == 0x8000u && (keep & 1u))", "(dropped == 0x8000u)"),

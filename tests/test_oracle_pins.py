@@ -534,16 +534,51 @@ def test_scaled_matmul_hand_worked_and_scale_shift():
 
 
 def test_scaled_matmul_e8m0_255_reading():
-    """Reading: an E8M0 of 255 makes its 32 elements NaN in the matmul."""
+    """Reading: the numerics page gives the consumer's dequant as
+    ldexpf(x, E8M0 - 127) with no exception, so a byte of 255 is the scale
+    2^128 in the matmul too. With a lhs column whose only nonzero block sits
+    under that byte, its results are exactly twice those under 254 (every
+    product doubles, so every partial sum doubles exactly); the other
+    columns do not change."""
     rng = np.random.default_rng(7)
     lhs, ls = _operand(rng, 16, 3, "e4m3fn", 125, 129)
     rhs, rs = _operand(rng, 16, 2, "e4m3fn", 125, 129)
-    base = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
-    assert not np.isnan(base).any()
-    ls[defcheck.scale_slot(1), 2] = 255          # row group 1 of lhs column 2
-    got = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
-    assert np.isnan(got[2]).all()
-    assert np.array_equal(np.delete(got, 2, axis=0), np.delete(base, 2, axis=0))
+    lhs[:8, 8:12] = 0                            # column 2 of lhs: row group 0 all zero
+    slot1 = defcheck.scale_slot(1)
+    ls[slot1, 2] = 254
+    at254 = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
+    ls[slot1, 2] = 255                           # row group 1 of lhs column 2
+    at255 = oracle.scaled_matmul(lhs, ls, rhs, rs, "e4m3fn")
+    assert not np.isnan(at255).any() and np.any(at255[2] != 0)
+    assert np.array_equal(at255[2], 2.0 * at254[2])
+    assert np.array_equal(np.delete(at255, 2, axis=0), np.delete(at254, 2, axis=0))
+
+
+@pytest.mark.parametrize("fmt", ("e4m3fn", "e5m2"))
+def test_scaled_matmul_and_dequantize_agree_on_element_values(fmt):
+    """Both consumers give an element the same value, decode(q) * 2^(E8M0 -
+    127): a one-hot rhs (R[k][n] = 1 if k == n) makes the matmul return the
+    lhs elements themselves, and rounded to fp32 they equal the dequantize's
+    values -- under every E8M0 byte 0..255, including those whose values
+    overflow fp32 (both then give the same infinity)."""
+    P, M = 8, 64                                  # K = 32, one block per column
+    rng = np.random.default_rng(70)
+    lhs, ls = _operand(rng, P, M, fmt, 0, 255)
+    ls[0, :] = np.arange(256)[rng.permutation(256)[:M]]
+    ls[0, :4] = (0, 1, 254, 255)
+    one = {"e4m3fn": 0x38, "e5m2": 0x3C}[fmt]
+    rhs = np.zeros((P, 4 * 32), np.uint8)
+    for k in range(32):
+        rhs[k // 4, 4 * k + k % 4] = one          # R[k][n = k] = 1.0 at E8M0 127
+    rs = np.zeros((P, 32), np.uint8)
+    rs[0, :] = 127
+    out = oracle.scaled_matmul(lhs, ls, rhs, rs, fmt)                # [M, K]
+    deq = oracle.dequantize(lhs, ls, P, 4 * M, fmt, "f32")          # [P, 4M]
+    L = _k_major(deq, P, M)                                          # [K, M]
+    with np.errstate(over="ignore"):
+        # compared as values: a sum of zeros is +0 where the element is -0
+        assert np.array_equal(out.T.astype(np.float32), L)
+    assert np.isinf(L[:, 3]).any() and np.isfinite(L[:, 0]).all() and (L[:, 0] != 0).any()
 
 
 # ------------------------------------------------------ quantize-on-produce
