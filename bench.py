@@ -58,7 +58,8 @@ cache size is then served largely from the cache.
 
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
-WRITE_SIZE readings into bytes.
+WRITE_SIZE readings into bytes. ``--floors`` times plain linear read, write
+and copy streams (torch's own kernels) for comparison.
 """
 from __future__ import annotations
 
@@ -120,17 +121,25 @@ def kernel_source_digest(op: str = "quantize") -> str:
 
 def recorded_traffic(workload: str, out: str, op: str = "quantize", res: str = ""):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current kernel sources, and where that figure comes from:
+    (bytes, source) or (None, source) -- the counters are read in runs of
+    their own (rocprofv3 --pmc), never inside this timed run."""
     tag = "%s_%s_%s" % (op, workload, out) + ("_" + res if res else "")
     path = os.path.join(PROFILES, "%s_hbm_traffic.txt" % tag)
+    digest = kernel_source_digest(op)
+    source = {"kind": "committed rocprofv3 --pmc summary (FETCH_SIZE, WRITE_SIZE runs)",
+              "file": os.path.relpath(path, ROOT), "kernel_source_sha256_16": digest,
+              "matches_current_sources": False}
     if not os.path.exists(path):
-        return None
+        source["file"] = None
+        return None, source
     text = open(path).read()
     m_src = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
     m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not m_src or not m_b or m_src.group(1) != kernel_source_digest(op):
-        return None
-    return float(m_b.group(1))
+    if not m_src or not m_b or m_src.group(1) != digest:
+        return None, source
+    source["matches_current_sources"] = True
+    return float(m_b.group(1)), source
 
 
 def make_input(workload: str, device):
@@ -384,19 +393,19 @@ def bench_matmul(args) -> int:
             mxq.scaled_matmul(dl, sl, dr, sr, fmt, res_t, out=out, stream=stream)
 
     total_ms, avg_ms = _time_steps(step, args.steps, args.warmup, stream)
-    traffic = recorded_traffic("%s-%dx%dx%d" % (fmt, M, N, K), qout if fused else args.res, args.op)
+    traffic, traffic_source = recorded_traffic("%s-%dx%dx%d" % (fmt, M, N, K), qout if fused else args.res, args.op)
     flops = 2.0 * M * N * K
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC_MATMUL_QUANTIZE if fused else METRIC_MATMUL, "value": round(value, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": fmt, "data": "synthetic",
+        "higher_is_better": True, "vs_baseline": None, "dtype": fmt, "data": "synthetic",
         "config": {"workload": "%s-%dx%dx%d-scaled-matmul%s" % (fmt, M, N, K, "-quantized-%s" % qout if fused else ""),
                    "M": M, "N": N, "K": K, "out": qout if fused else args.res, "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel_avg_us": round(avg_ms * 1e3, 3)},
+                     "traffic_source": traffic_source, "kernel_avg_us": round(avg_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
     if compare:
@@ -427,6 +436,28 @@ def copy_calibration(steps: int, warmup: int) -> None:
                       "copy_GBps": round(4 * n / ms / 1e6, 1)}), flush=True)
 
 
+def floors(steps: int, warmup: int) -> None:
+    """Plain linear streams with torch's own kernels, for comparison with
+    the library's kernels: a read of 2 GiB (a sum), writes of 1 GiB and
+    2 GiB (a fill) and a 2 GiB copy; each timed over `steps` back-to-back
+    launches between two events on the current stream."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    src = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda")      # 2 GiB
+    dst1 = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")       # 1 GiB
+    dst2 = torch.empty(1 << 30, dtype=torch.bfloat16, device="cuda")    # 2 GiB
+    cases = [("read_2GiB_sum", lambda: src.sum(dtype=torch.float32), 2 << 30),
+             ("write_1GiB_fill", lambda: dst1.fill_(7), 1 << 30),
+             ("write_2GiB_fill", lambda: dst2.fill_(3.0), 2 << 30),
+             ("copy_2GiB", lambda: dst2.copy_(src), 4 << 30)]
+    out = {}
+    for name, fn, nbytes in cases:
+        total_ms, avg_ms = _time_steps(fn, steps, warmup, stream)
+        out[name] = {"us": round(avg_ms * 1e3, 2), "GBps": round(nbytes / (avg_ms * 1e-3) / 1e9, 1)}
+    print(json.dumps({"floors": out, "steps": steps, "warmup": warmup}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +477,8 @@ def main() -> int:
                     help="flushed: read 512 MiB between launches and time the launches alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--floors", action="store_true",
+                    help="time plain linear read / write / copy streams (torch kernels) instead")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -466,6 +499,9 @@ def main() -> int:
         return 1
     if args.copy_calibration:
         copy_calibration(args.steps, args.warmup)
+        return 0
+    if args.floors:
+        floors(args.steps, args.warmup)
         return 0
     if args.op in ("matmul", "matmul_quantize"):
         return bench_matmul(args)
@@ -517,11 +553,11 @@ def main() -> int:
     value = nbytes * args.steps / (total_ms * 1e-3) / 1e9
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
     if args.op == "quantize":
-        traffic = recorded_traffic(args.workload, out)
+        traffic, traffic_source = recorded_traffic(args.workload, out)
     elif args.op == "quantize_axis":
-        traffic = recorded_traffic(args.workload, out, "quantize_axis", "dim%d" % args.dim)
+        traffic, traffic_source = recorded_traffic(args.workload, out, "quantize_axis", "dim%d" % args.dim)
     else:
-        traffic = recorded_traffic(args.workload, out, "dequantize", args.res)
+        traffic, traffic_source = recorded_traffic(args.workload, out, "dequantize", args.res)
 
     config = {"workload": args.workload, "P": P, "F": F, "in": spec["in_dtype"], "out": out,
               "bytes_per_step": nbytes, "elements_per_step": P * F}
@@ -542,7 +578,6 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(total_ms / args.steps, 5),
         "higher_is_better": True,
-        "scaling": "weak",
         "vs_baseline": None,
         "dtype": out if args.op == "dequantize" else spec["in_dtype"],
         "data": "synthetic",
@@ -551,7 +586,7 @@ def main() -> int:
         "elements_per_s": round(P * F * args.steps / (total_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel_avg_us": round(avg_launch_ms * 1e3, 3)},
+                     "traffic_source": traffic_source, "kernel_avg_us": round(avg_launch_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -187,8 +187,12 @@ def quantize(x: torch.Tensor, out_dtype: str = "e4m3fn", data_out: torch.Tensor 
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
-        _check(lib.mxq_quantize_ex(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, flags, data_out.data_ptr(),
-                                   scale_out.data_ptr(), stream.cuda_stream))
+        if flags == 0:    # the contract's own entry point
+            _check(lib.mxq_quantize(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, data_out.data_ptr(),
+                                    scale_out.data_ptr(), stream.cuda_stream))
+        else:
+            _check(lib.mxq_quantize_ex(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, flags, data_out.data_ptr(),
+                                       scale_out.data_ptr(), stream.cuda_stream))
     return data_out, scale_out
 
 

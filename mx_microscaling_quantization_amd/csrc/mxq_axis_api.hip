@@ -13,7 +13,7 @@ namespace {
 using mxq_host::check_shape;
 using mxq_host::emax_of;
 using mxq_host::kMaxF;
-using mxq_host::kMaxWorkgroups;
+using mxq_host::grid_fits;
 
 typedef void (*down_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, int, uint32_t);
 typedef void (*along_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint64_t, uint32_t, int, uint32_t,
@@ -112,14 +112,14 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
     if (down) {
         width = (O % 4 == 0) ? 4 : (O % 2 == 0) ? 2 : 1; // columns per thread
         tiles = (O / width + threads - 1) / threads;     // per 32-row band
-        if (K / 32 > kMaxWorkgroups / tiles)
+        if (!grid_fits(K / 32, tiles, threads))
             return MXQ_E_OVERFLOW;
         grid = (K / 32) * tiles;
     } else {
         width = O % 4 != 0;                                   // rows of the view not 16-byte aligned
         tiles = (O + mxq::kAlongRows - 1) / mxq::kAlongRows; // row tiles
         const int64_t ktiles = (K / 32 + 1) / 2;              // two blocks per tile
-        if (ktiles > kMaxWorkgroups / tiles)
+        if (!grid_fits(ktiles, tiles, 64 * mxq::kAlongWaves))
             return MXQ_E_OVERFLOW;
         grid = ktiles * tiles;
     }

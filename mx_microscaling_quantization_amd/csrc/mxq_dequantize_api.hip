@@ -12,7 +12,7 @@ namespace {
 using mxq_host::check_shape;
 using mxq_host::emax_of;
 using mxq_host::kMaxF;
-using mxq_host::kMaxWorkgroups;
+using mxq_host::grid_fits;
 
 // One 64-lane wave per workgroup, non-temporal loads and stores (the data
 // streams through once), as for the quantize. When the result rows do not
@@ -82,7 +82,7 @@ int mxq_dequantize_ex(const void *data, const void *scale_in, int64_t P, int64_t
     const int64_t nstrips = F / (4 * nb);
     const int64_t tiles_per_group = (nstrips + kThreads - 1) / kThreads;
     const int64_t groups = P / 8;
-    if (groups > kMaxWorkgroups / tiles_per_group)
+    if (!grid_fits(groups, tiles_per_group, kThreads))
         return MXQ_E_OVERFLOW;
 
     const bool aligned = F * (res_dtype == MXQ_RES_F32 ? 4 : 2) % 128 == 0; // result row pitch

@@ -12,7 +12,16 @@ namespace mxq_host {
 // The kernel indexes strips, workgroups and per-row offsets with 32-bit
 // counts and 64-bit byte offsets; these bounds keep every count in range.
 constexpr int64_t kMaxF = (int64_t)1 << 31;
-constexpr int64_t kMaxWorkgroups = ((int64_t)1 << 31) - 1;
+
+// A launch's grid: `a` x `b` workgroups of `threads` threads. The dispatch
+// packet counts work-items (workgroups x threads) in 32 bits, so a grid
+// fits only when that product is at most 2^32 - 1 (which also keeps the
+// workgroup count, a 32-bit kernel argument, in range).
+constexpr int64_t kMaxWorkItems = ((int64_t)1 << 32) - 1;
+inline bool grid_fits(int64_t a, int64_t b, int64_t threads)
+{
+    return a >= 0 && b > 0 && a <= kMaxWorkItems / threads / b;
+}
 
 // EMAX of an output format ("MX Microscaling: Quantize, Block-Scaling and
 // E8M0", The EMAX Table).

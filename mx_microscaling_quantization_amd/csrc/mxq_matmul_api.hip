@@ -13,7 +13,7 @@ namespace {
 using mxq_host::check_shape;
 using mxq_host::emax_of;
 using mxq_host::kMaxF;
-using mxq_host::kMaxWorkgroups;
+using mxq_host::grid_fits;
 
 typedef void (*mm_kernel_fn)(const uint8_t *, const uint8_t *, const uint8_t *, const uint8_t *, uint32_t, uint32_t,
                              uint32_t, uint32_t, uint32_t, void *, uint8_t *, int);
@@ -57,7 +57,7 @@ int mm_launch(int fmt, int epi, const void *lhs, const void *lhs_scale, const vo
 {
     const int64_t tiles_m = (M + mxq::kMmTile - 1) / mxq::kMmTile;
     const int64_t tiles_n = (N + mxq::kMmTile - 1) / mxq::kMmTile;
-    if (tiles_m > (((int64_t)1 << 31) - 1) / tiles_n)
+    if (!grid_fits(tiles_m, tiles_n, mxq::kMmThreads))
         return MXQ_E_OVERFLOW;
     mm_kernel_fn k = fmt == MXQ_OUT_E4M3FN ? mm_pick_epi<mxq::kOutE4M3FN>(epi) : mm_pick_epi<mxq::kOutE5M2>(epi);
     const uint8_t *a0 = (const uint8_t *)lhs;

@@ -48,9 +48,9 @@ enum { kEpiF32 = 0, kEpiBF16 = 1, kEpiMx = 2 };
 __device__ __forceinline__ uint32_t mm_bf16_bits(float v)
 {
     const uint32_t bits = __float_as_uint(v);
-    if ((bits & 0x7FFFFFFFu) > 0x7F800000u)
-        return (bits >> 16) | 0x40u;
-    return (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+    const uint32_t nearest = (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (bits >> 16) | 0x40u;
+    return (bits & 0x7FFFFFFFu) > 0x7F800000u ? quiet : nearest;   // a select, no branch
 }
 
 // ----------------------------------------------------------------------------
@@ -252,7 +252,179 @@ __device__ __forceinline__ void mm_quantize_epilogue(const f32x16_t (&acc)[2][4]
     }
 }
 
-// M and N are multiples of 4 (checked on the host), so a row's 4 adjacent
+// The lane's 8 operand dwords with the blocks whose flag is clear zeroed:
+// dwords 0..3 belong to K block 0 of the step, 4..7 to block 1.
+__device__ __forceinline__ i32x8_t mm_keep_blocks(const i32x8_t &v, bool block0, bool block1)
+{
+    i32x8_t o;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        o[k] = block0 ? v[k] : 0;
+        o[k + 4] = block1 ? v[k + 4] : 0;
+    }
+    return o;
+}
+
+// The K step of one A sub-tile against the wave's 4 B sub-tiles where scale
+// bytes may be 255. An E8M0 byte e stands for 2^(e - 127) for every e, 255
+// (2^128) included -- the consumer's dequant is ldexpf(x, E8M0 - 127) --
+// but the matrix cores read a scale byte of 0xFF as NaN. So every 255 is fed
+// as 254 (2^127), which leaves each flagged block's products at half their
+// value per flagged side. Lane (i, h) carries the scale of K block h of its
+// row (column) i, so the flag of block 1 - h comes from lane (i, 1 - h).
+// With A' and B' the operands keeping only their flagged blocks (dwords
+// 0..3 are block 0, 4..7 block 1), the step adds (A, B) + (A', B) +
+// (A', B') + (A, B'): a block flagged on one side counts twice, on both
+// sides four times, an unflagged one once.
+template <int F>
+__device__ __forceinline__ void mm_step_255(f32x16_t (&acc)[4], const i32x8_t &aop, const i32x8_t (&bop)[4],
+                                            uint32_t as, uint32_t bs, uint32_t h)
+{
+    // flag bits: 2 u + j for block j of B sub-tile u, 8 + j for block j of A
+    uint32_t own = as == 255u ? 1u << 8 : 0u, bclamp = 0;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const uint32_t byte = (bs >> (8 * u)) & 0xFFu;
+        own |= (byte == 255u ? 1u : 0u) << (2 * u);
+        bclamp |= (byte == 255u ? 254u : byte) << (8 * u);
+    }
+    const uint32_t other = (uint32_t)__shfl_xor((int)own, 32);
+    const uint32_t flags = h ? (own << 1) | other : own | (other << 1);
+    const int sa = (int)min(as, 254u);
+    const i32x8_t ta = mm_keep_blocks(aop, (flags >> 8) & 1u, (flags >> 9) & 1u);
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int sb = (int)(bclamp >> (8 * u));   // byte u in byte 0, op_sel 0
+        const i32x8_t tb = mm_keep_blocks(bop[u], (flags >> (2 * u)) & 1u, (flags >> (2 * u + 1)) & 1u);
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[u], acc[u], F, F, 0, sa, 0, sb);
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ta, bop[u], acc[u], F, F, 0, sa, 0, sb);
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ta, tb, acc[u], F, F, 0, sa, 0, sb);
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, tb, acc[u], F, F, 0, sa, 0, sb);
+    }
+}
+
+// A buffer over the K step `step` of an operand from column c0 (as the
+// copies use): rows past P and bytes past the operand read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mm_step_rsrc(const MmSource &s, uint32_t P, uint32_t step)
+{
+    const uint32_t rows_left = min(P - step * kMmStepRows, kMmStepRows);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(s.data + (uint64_t)step * kMmStepRows * s.pitch), (short)0,
+                                             (int)(rows_left * s.pitch - s.col_bytes), kMmBufferFlags);
+}
+
+// The rare path: a wave's whole 64 x 128 part of the tile computed again,
+// one A sub-tile at a time, with mm_step_255, the operands read straight
+// from global memory in the main loop's lane mapping (lane (i, h): A
+// container c0a + 2 i + a, B containers c0b + 4 i + u, rows 4 h .. 4 h + 3 and
+// 8 + 4 h .. 11 + 4 h of each K step). No LDS and no barrier: the other
+// waves go on undisturbed.
+template <int F>
+__device__ __forceinline__ void mm_tile_255(f32x16_t (&acc)[2][4], const uint8_t *lhs, const uint8_t *lhs_scale,
+                                            const uint8_t *rhs, const uint8_t *rhs_scale, uint32_t P, uint32_t M,
+                                            uint32_t N, uint32_t c0a, uint32_t c0b, uint32_t dense, uint32_t i,
+                                            uint32_t h)
+{
+    MmSource sa, sb;
+    mm_source(sa, lhs, lhs_scale, M, c0a);
+    mm_source(sb, rhs, rhs_scale, N, c0b);
+    const uint32_t groups = P / 8;
+    const uint32_t nsteps = (P + kMmStepRows - 1) / kMmStepRows;
+    const uint32_t lane_a = 4u * h * sa.pitch + 8u * i, lane_b = 4u * h * sb.pitch + 16u * i;
+    // every sum restarts from zero at once, so no earlier value stays live
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            acc[a][u] = f32x16_t{};
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+        for (uint32_t s = 0; s < nsteps; s++) {
+            const __amdgpu_buffer_rsrc_t ra = mm_step_rsrc(sa, P, s), rb = mm_step_rsrc(sb, P, s);
+            // row 4 h + (v & 3) (+ 8 for v >= 4): the lane's part of the
+            // offset in a vector register, the row's in a scalar one
+            i32x8_t aop, bop[4];
+#pragma unroll
+            for (int v = 0; v < 8; v++) {
+                const uint32_t vrow = (v < 4 ? 0u : 8u) + (v & 3);
+                aop[v] = (int)__builtin_amdgcn_raw_buffer_load_b32(ra, lane_a + 4u * a, vrow * sa.pitch, 0);
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    bop[u][v] = (int)__builtin_amdgcn_raw_buffer_load_b32(rb, lane_b + 4u * u, vrow * sb.pitch, 0);
+            }
+            // this lane's scales: K block 2 s + h of its A container and B
+            // containers; a block past P / 8 has zero data and gets 127
+            const uint32_t g = 2u * s + h;
+            uint32_t as = 0x7Fu, bs = 0x7F7F7F7Fu;
+            if (g < groups) {
+                // the scale row from column c0 on, as the copies read it:
+                // containers past the operand's last read as zero
+                const uint64_t srow = dense ? g : (g & 3u) + 32u * (g >> 2);
+                const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(sa.scale + srow * M), (short)0, (int)sa.scale_cols, kMmBufferFlags);
+                const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(sb.scale + srow * N), (short)0, (int)sb.scale_cols, kMmBufferFlags);
+                as = __builtin_amdgcn_raw_buffer_load_b8(rsa, 2u * i + a, 0, 0);
+                bs = __builtin_amdgcn_raw_buffer_load_b32(rsb, 4u * i, 0, 0);
+            }
+            mm_step_255<F>(acc[a], aop, bop, as, bs, h);
+        }
+    }
+}
+
+// Store a wave's sums (64 x 128 from row wm0, column wn0): f32, bf16 or MX
+// quantized. M and N are multiples of 4 (checked on the host), so a row's 4
+// adjacent results are one aligned 16-byte (f32) or 8-byte (bf16) store.
+template <int EPI>
+__device__ __forceinline__ void mm_epilogue(const f32x16_t (&acc)[2][4], uint32_t wm0, uint32_t wn0, uint32_t M,
+                                            uint32_t N, void *__restrict__ out, uint8_t *__restrict__ out_scale,
+                                            int emax_bias, uint32_t dense, uint32_t i, uint32_t h)
+{
+    const uint32_t col = wn0 + 4u * i;
+    const uint32_t row0 = wm0 + 8u * h;   // + 16 (r >> 2) + 2 (r & 3) + a
+    if constexpr (EPI >= kEpiMx) {
+        mm_quantize_epilogue<EPI - kEpiMx>(acc, row0, col, M, N, reinterpret_cast<uint8_t *>(out), out_scale,
+                                            emax_bias, dense);
+        return;
+    }
+    if (col >= N)
+        return;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const uint32_t m = row0 + 16u * (r >> 2) + 2u * (r & 3) + a;
+            if (m >= M)
+                continue;
+            const uint64_t o = (uint64_t)m * N + col;
+            if constexpr (EPI == kEpiF32)
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + o) =
+                    float4{acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]};
+            else
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + o) =
+                    uint2{mm_bf16_bits(acc[a][0][r]) | mm_bf16_bits(acc[a][1][r]) << 16,
+                          mm_bf16_bits(acc[a][2][r]) | mm_bf16_bits(acc[a][3][r]) << 16};
+        }
+}
+
+// The rare path as a function of its own (not inlined): its registers are
+// allocated apart from the main loop's, and nothing of the caller but a few
+// scalars is live across the call. It computes the wave's part with
+// mm_tile_255 and stores it.
+template <int F, int EPI>
+__device__ __attribute__((noinline)) void mm_rare_part(const uint8_t *lhs, const uint8_t *lhs_scale,
+                                                       const uint8_t *rhs, const uint8_t *rhs_scale, uint32_t P,
+                                                       uint32_t M, uint32_t N, uint32_t wm0, uint32_t wn0,
+                                                       uint32_t dense, void *out, uint8_t *out_scale, int emax_bias)
+{
+    const uint32_t lane = __lane_id();
+    const uint32_t i = lane & 31u, h = lane >> 5;
+    f32x16_t acc[2][4];
+    mm_tile_255<F>(acc, lhs, lhs_scale, rhs, rhs_scale, P, M, N, wm0, wn0, dense, i, h);
+    mm_epilogue<EPI>(acc, wm0, wn0, M, N, out, out_scale, emax_bias, dense, i, h);
+}
+
+// The kernel.
+
 // results are one aligned 16-byte (f32) or 8-byte (bf16) store.
 template <int FMT, int EPI>
 __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
@@ -373,31 +545,28 @@ __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
         __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_waitcnt(kWaitAllCopies);
 
-    const uint32_t col = n0 + wn + 4u * i;
-    const uint32_t row0 = m0 + wm + 8u * h;   // + 16 (r >> 2) + 2 (r & 3) + a
-    if constexpr (EPI >= kEpiMx) {
-        mm_quantize_epilogue<EPI - kEpiMx>(acc, row0, col, M, N, reinterpret_cast<uint8_t *>(out), out_scale,
-                                            emax_bias, dense);
-        return;
+    // The matrix cores read a scale byte of 255 as NaN, where it stands for
+    // 2^128. A sum that is not finite may come from one, so the wave then
+    // computes its part again on the rare path, which gives every byte its
+    // value (and any other non-finite sum the same value again), and stores
+    // that.
+    bool finite = true;
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                finite = finite && __builtin_isfinite(acc[a][u][r]);
+
+    if (__builtin_amdgcn_ballot_w64(!finite) != 0) {
+        mm_rare_part<F, EPI>(lhs, lhs_scale, rhs, rhs_scale, P, M, N, m0 + wm, n0 + wn, dense, out, out_scale,
+                             emax_bias);
+        // the wave ends here (no path back to the epilogue below, whose
+        // sums would otherwise have to stay live across this branch)
+        __builtin_amdgcn_endpgm();
     }
-    if (col >= N)
-        return;
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-#pragma unroll
-        for (int a = 0; a < 2; a++) {
-            const uint32_t m = row0 + 16u * (r >> 2) + 2u * (r & 3) + a;
-            if (m >= M)
-                continue;
-            const uint64_t o = (uint64_t)m * N + col;
-            if constexpr (EPI == kEpiF32)
-                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + o) =
-                    float4{acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]};
-            else
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + o) =
-                    uint2{mm_bf16_bits(acc[a][0][r]) | mm_bf16_bits(acc[a][1][r]) << 16,
-                          mm_bf16_bits(acc[a][2][r]) | mm_bf16_bits(acc[a][3][r]) << 16};
-        }
+    mm_epilogue<EPI>(acc, m0 + wm, n0 + wn, M, N, out, out_scale, emax_bias, dense, i, h);
 }
 
 } // namespace mxq

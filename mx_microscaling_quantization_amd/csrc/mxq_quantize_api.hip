@@ -13,7 +13,7 @@ namespace {
 using mxq_host::check_shape;
 using mxq_host::emax_of;
 using mxq_host::kMaxF;
-using mxq_host::kMaxWorkgroups;
+using mxq_host::grid_fits;
 
 // Workgroups of one wave stream this kernel fastest, with a residency cap
 // once the tensor outgrows the cache: at most 10 waves per CU for FP8 output
@@ -104,7 +104,7 @@ int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_
     const int64_t tiles_per_band = (nstrips + threads - 1) / threads;
     const int64_t groups = P / 8;
     const int64_t bands = (groups + kGroupsPerThread - 1) / kGroupsPerThread;
-    if (bands > kMaxWorkgroups / tiles_per_band)
+    if (!grid_fits(bands, tiles_per_band, threads))
         return MXQ_E_OVERFLOW;
 
     kernel_fn k = in_dtype == MXQ_IN_BF16

@@ -110,6 +110,31 @@ def test_validation_errors_before_launch():
     assert _call(good, 16, 8, 1, 1, good, good + 1) == e["MXQ_E_ALIGN"]
 
 
+def test_launch_over_2_to_32_work_items_is_refused():
+    """A valid narrow tensor whose grid would exceed the 32-bit work-item
+    count of a dispatch is refused before any launch (MXQ_E_OVERFLOW), for
+    every entry point; just under the limit the same shapes pass the size
+    check (they then fail on the fake pointers' alignment, still before a
+    launch)."""
+    e = _header_enums()
+    lib = mxq.load()
+    good = 4096
+    # quantize: F = 4 puts one strip in a 64-thread workgroup per row group
+    assert _call(good, 1 << 31, 4, 0, 0, good, good) == e["MXQ_E_OVERFLOW"]
+    assert lib.mxq_quantize_ex(good, 1 << 31, 4, 0, 2, 0, good, good, None) == e["MXQ_E_OVERFLOW"]
+    assert _call(good, 8 * ((1 << 26) - 1), 4, 0, 0, good + 8, good) == e["MXQ_E_ALIGN"]
+    # dequantize: same geometry
+    assert _dq(good, good, 1 << 31, 4, 0, 1, good) == e["MXQ_E_OVERFLOW"]
+    assert _dq(good, good, 8 * ((1 << 26) - 1), 4, 0, 1, good + 8) == e["MXQ_E_ALIGN"]
+    # quantize_axis down the columns: a 32-row band per workgroup row
+    assert lib.mxq_quantize_axis(good, 1 << 32, 4, 0, 0, -2, 0, good, good, None) == e["MXQ_E_OVERFLOW"]
+    # along the rows: 256-row tiles x 2 blocks
+    assert lib.mxq_quantize_axis(good, 256, 1 << 33, 0, 0, -1, 0, good, good, None) == e["MXQ_E_OVERFLOW"]
+    # the matmul: 256 x 256 tiles of 512 threads
+    big = mxq.MATMUL_MAX_COLS if hasattr(mxq, "MATMUL_MAX_COLS") else 33554176
+    assert lib.mxq_scaled_matmul(good, good, good, good, 8, big, big, 0, 0, 0, good, None) == e["MXQ_E_OVERFLOW"]
+
+
 def _dq(d, s, P, F, fmt, res, out):
     return mxq.load().mxq_dequantize(d, s, P, F, fmt, res, out, None)
 

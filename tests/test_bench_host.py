@@ -51,13 +51,18 @@ def test_recorded_traffic_follows_the_source_digest(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     tag = "quantize_wl_e4m3fn"
     path = tmp_path / ("%s_hbm_traffic.txt" % tag)
-    assert bench.recorded_traffic("wl", "e4m3fn") is None                # no summary
+    t, src = bench.recorded_traffic("wl", "e4m3fn")
+    assert t is None and src["file"] is None                            # no summary
     path.write_text(_summary(bench.kernel_source_digest("quantize"), 3254863572))
-    assert bench.recorded_traffic("wl", "e4m3fn") == 3254863572.0         # current sources
+    t, src = bench.recorded_traffic("wl", "e4m3fn")
+    assert t == 3254863572.0 and src["matches_current_sources"]          # current sources
+    assert src["kernel_source_sha256_16"] == bench.kernel_source_digest("quantize")
+    assert src["file"].endswith("quantize_wl_e4m3fn_hbm_traffic.txt") and "--pmc" in src["kind"]
     path.write_text(_summary("0123456789abcdef", 3254863572))
-    assert bench.recorded_traffic("wl", "e4m3fn") is None                # stale sources
+    t, src = bench.recorded_traffic("wl", "e4m3fn")
+    assert t is None and not src["matches_current_sources"]              # stale sources
     path.write_text("kernel_source_sha256_16: %s\n" % bench.kernel_source_digest("quantize"))
-    assert bench.recorded_traffic("wl", "e4m3fn") is None                # no byte count
+    assert bench.recorded_traffic("wl", "e4m3fn")[0] is None             # no byte count
 
 
 def test_recorded_traffic_digest_is_per_op(tmp_path, monkeypatch):
@@ -66,7 +71,13 @@ def test_recorded_traffic_digest_is_per_op(tmp_path, monkeypatch):
         _summary(bench.kernel_source_digest("quantize"), 1.0))
     # a dequantize summary carrying the quantize digest is not accepted
     if bench.kernel_source_digest("quantize") != bench.kernel_source_digest("dequantize"):
-        assert bench.recorded_traffic("wl", "e4m3fn", "dequantize", "bf16") is None
+        assert bench.recorded_traffic("wl", "e4m3fn", "dequantize", "bf16")[0] is None
+
+
+def test_bench_line_has_no_scaling_key():
+    """One GPU: no weak/strong scaling claim on the line."""
+    text = open(os.path.join(ROOT, "bench.py")).read()
+    assert '"scaling"' not in text
 
 
 def test_every_kernel_source_exists():

@@ -121,9 +121,13 @@ def test_axis_empty_is_noop():
 @pytest.mark.parametrize("dim", [-2, -1])
 def test_axis_full_size(dim):
     """The 1.07 G-element bench input quantized along each axis: all bytes
-    against the plain quantize of the torch-built view (itself checked
-    against the oracle at this size), and one 32-row band of the block axis
-    against the oracle."""
+    against the plain GPU quantize of the torch-built view, and all bytes
+    (data and placed scale rows) against the oracle's quantize_axis, run
+    over slabs of whole 128-element stretches of the block axis (32 view
+    rows, so each slab's scale rows are the global ones shifted) on the
+    host's threads."""
+    from bands import run_bands
+
     progress("quantize_axis full size dim=%d: input" % dim)
     x = workloads.colscaled_bf16_device(device="cuda")
     R, C = x.shape
@@ -135,20 +139,30 @@ def test_axis_full_size(dim):
     del v
     assert torch.equal(d, d_ref)
     P = s.shape[0]
-    placed = torch.from_numpy((np.arange(P // 8) % 4) + 32 * (np.arange(P // 8) // 4)).cuda()
-    assert torch.equal(s[placed], s_ref[placed])
-    progress("quantize_axis full size dim=%d: sampled band vs oracle" % dim)
-    rng = np.random.default_rng(dim + 10)
-    for _ in range(2):
-        if dim == -2:
-            band = int(rng.integers(R // 32))
-            bits = x[32 * band:32 * band + 32].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-            ref_d, ref_s = oracle.quantize_axis(bits, "bf16", "e4m3fn", -2)
-            assert np.array_equal(d[8 * band:8 * band + 8].cpu().numpy(), ref_d)
-        else:
-            band = int(rng.integers(C // 32))
-            bits = x[:, 32 * band:32 * band + 32].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-            ref_d, ref_s = oracle.quantize_axis(bits, "bf16", "e4m3fn", -1)
-            assert np.array_equal(d[8 * band:8 * band + 8].cpu().numpy(), ref_d)
-        slot = (band % 4) + 32 * (band // 4)
-        assert np.array_equal(s[slot].cpu().numpy(), ref_s[0])
+    placed = (np.arange(P // 8) % 4) + 32 * (np.arange(P // 8) // 4)
+    assert torch.equal(s[torch.from_numpy(placed).cuda()], s_ref[torch.from_numpy(placed).cuda()])
+    del d_ref, s_ref
+    progress("quantize_axis full size dim=%d: copy to host" % dim)
+    bits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    del x
+    hd, hs = d.cpu().numpy(), s.cpu().numpy()
+    del d, s
+    oracle.quantize_axis(bits[:32, :32].copy(), "bf16", "e4m3fn", dim)   # load the library before the threads
+    progress("quantize_axis full size dim=%d: whole-tensor oracle compare" % dim)
+    K = R if dim == -2 else C
+
+    def check(v0, v1):
+        # view rows [v0, v1) = block-axis elements [4 v0, 4 v1)
+        k0, k1 = 4 * v0, 4 * v1
+        part = bits[k0:k1] if dim == -2 else np.ascontiguousarray(bits[:, k0:k1])
+        ref_d, ref_s = oracle.quantize_axis(part, "bf16", "e4m3fn", dim)
+        if not np.array_equal(hd[v0:v1], ref_d):
+            r, c = np.argwhere(hd[v0:v1] != ref_d)[0]
+            return "data differs at view (%d, %d)" % (v0 + r, c)
+        rows = placed[(placed >= 0) & (placed < v1 - v0)]
+        if not np.array_equal(hs[v0 + rows], ref_s[rows]):
+            return "scale rows differ in view rows [%d, %d)" % (v0, v1)
+        return None
+
+    bad = run_bands(K // 4, check)
+    assert not bad, "%d slabs differ; first: %s" % (len(bad), bad[0])

@@ -13,9 +13,9 @@ from conftest import progress
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-TOP_KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+TOP_KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
             "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"}
-ROOF_KEYS = {"bound", "achieved", "peak", "unit", "frac", "traffic"}
+ROOF_KEYS = {"bound", "achieved", "peak", "unit", "frac", "traffic", "traffic_source"}
 
 
 def _bench(*args):
@@ -32,13 +32,16 @@ def _check_common(d, steps, warmup):
     assert TOP_KEYS <= set(d), TOP_KEYS - set(d)
     assert d["n_gpus"] == 1 and d["steps"] == steps and d["warmup"] == warmup
     assert d["value"] > 0 and d["ms_per_step"] > 0
-    assert d["higher_is_better"] is True and d["scaling"] == "weak" and d["data"] == "synthetic"
+    assert d["higher_is_better"] is True and "scaling" not in d and d["data"] == "synthetic"
     assert "workload" in d["config"]
     roof = d["roofline"]
     assert ROOF_KEYS <= set(roof), ROOF_KEYS - set(roof)
     assert roof["peak"] > 0 and roof["achieved"] > 0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert 0 < roof["frac"] < 1.2
+    src = roof["traffic_source"]
+    assert "--pmc" in src["kind"] and src["kernel_source_sha256_16"]
+    assert (roof["traffic"] is None) or src["matches_current_sources"]
 
 
 def test_quantize_line_with_cpu_baselines():

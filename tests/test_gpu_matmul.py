@@ -10,7 +10,10 @@ accumulator with fp32 round-to-nearest additions. So for each result
 and for a bf16 result half a bf16 ulp more: 2^-8 * (|exact| + that bound).
 The block maximum is bounded by max_k |L[k][m]| * max_k |R[k][n]| over the
 block. A wrong layout, pairing or scale breaks this bound by orders of
-magnitude.
+magnitude. A block under an E8M0 of 255 is summed in up to four additions
+(the kernel's rare path), so tests with such blocks count 4 per block.
+Exact results beyond the fp32 range must come back as infinities of their
+sign.
 """
 import numpy as np
 import pytest
@@ -41,46 +44,66 @@ def make_operand(P: int, C: int, fmt: str, seed: int, dense: bool = False):
     return d, s, d.cpu().numpy(), s.cpu().numpy()
 
 
-def bound(L: np.ndarray, R: np.ndarray, res) -> np.ndarray:
-    """The error bound above for [K, M] and [K, N] dequantized operands."""
+def bound(L: np.ndarray, R: np.ndarray, res, ref: np.ndarray, adds_per_block: int = 1) -> np.ndarray:
+    """The error bound above for [K, M] and [K, N] dequantized operands
+    (float64, exact) and the exact result ``ref``."""
     K = L.shape[0]
     with np.errstate(invalid="ignore", over="ignore"):
         aL, aR = np.abs(L), np.abs(R)
         absum = aL.T @ aR
         Lmax = aL.reshape(K // 32, 32, -1).max(axis=1)      # [K/32, M]
         Rmax = aR.reshape(K // 32, 32, -1).max(axis=1)      # [K/32, N]
-        tol = 31 * 2.0 ** -12 * (Lmax.T @ Rmax) + (K // 32 + 2) * 2.0 ** -24 * absum
+        tol = 31 * 2.0 ** -12 * (Lmax.T @ Rmax) + (adds_per_block * K // 32 + 2) * 2.0 ** -24 * absum
         if res == torch.bfloat16:
-            tol = tol + 2.0 ** -8 * (absum + tol)
+            tol = tol + 2.0 ** -8 * (np.abs(ref) + tol)
     return np.nan_to_num(tol, nan=0.0)
 
 
-def check(P, M, N, fmt, res, dense=False, seed=0, scale_patch=None):
-    layout = "dense" if dense else "image"
-    dl, sl, hl, hsl = make_operand(P, M, fmt, seed * 2 + 1, dense)
-    dr, sr, hr, hsr = make_operand(P, N, fmt, seed * 2 + 2, dense)
-    if scale_patch is not None:
-        scale_patch(sl, hsl)
-    out = mxq.scaled_matmul(dl, sl, dr, sr, fmt, res, dense_scale=dense)
-    torch.cuda.synchronize()
-    got = out.float().cpu().numpy().astype(np.float64)
-    ref = oracle.scaled_matmul(hl, hsl, hr, hsr, fmt, layout=layout)
-    with np.errstate(invalid="ignore", over="ignore"):
-        L = _k_major(oracle.dequantize(hl, hsl, P, 4 * M, fmt, "f32", layout=layout).astype(np.float64), P, M)
-        R = _k_major(oracle.dequantize(hr, hsr, P, 4 * N, fmt, "f32", layout=layout).astype(np.float64), P, N)
-    tol = bound(L, R, res)
+def values64(data: np.ndarray, scale: np.ndarray, P: int, C: int, fmt: str, layout: str = "image") -> np.ndarray:
+    """The [K, C] operand matrix in float64: decode(q) * 2^(E8M0 - 127),
+    exact for every byte (no fp32 rounding or overflow)."""
+    codes = oracle.decode(data, fmt).reshape(P, 4 * C)
+    rows = np.arange(P) // 8
+    srow = rows if layout == "dense" else (rows % 4) + 32 * (rows // 4)
+    e = scale[srow].astype(np.int64)                       # [P, C]
+    vals = codes * np.ldexp(1.0, np.repeat(e, 4, axis=1) - 127)
+    return _k_major(vals, P, C)
+
+
+FP32_OVERFLOW = (2.0 - 2.0 ** -24) * 2.0 ** 127       # exact values from here round to Inf
+
+
+def compare(got: np.ndarray, ref: np.ndarray, tol: np.ndarray):
     nan_ref = np.isnan(ref)
     assert np.array_equal(np.isnan(got), nan_ref), "NaN positions differ"
-    err = np.abs(got - ref)
-    ok = (err <= tol) | nan_ref
-    with np.errstate(invalid="ignore", divide="ignore"):
-        rel = err[~nan_ref] / np.maximum(np.abs(ref[~nan_ref]), 1e-300)
+    over = ~nan_ref & (np.abs(ref) >= FP32_OVERFLOW)
+    assert np.array_equal(got[over], np.copysign(np.inf, ref[over])), "results beyond fp32 must be infinities"
+    fin = ~nan_ref & ~over
+    with np.errstate(invalid="ignore"):
+        err = np.abs(got - ref)
+    ok = (err <= tol) | ~fin
+    rel = err[fin] / np.maximum(np.abs(ref[fin]), 1e-300)
     if rel.size:
         progress("relative error vs exact: median %.3g max %.3g" % (np.median(rel), rel.max()))
     if not ok.all():
         m, n = np.argwhere(~ok)[0]
         raise AssertionError("%d of %d results outside the bound; first [%d,%d]: gpu %r exact %r bound %r"
                              % (int((~ok).sum()), ok.size, m, n, got[m, n], ref[m, n], tol[m, n]))
+
+
+def check(P, M, N, fmt, res, dense=False, seed=0, scale_patch=None, adds_per_block=1):
+    layout = "dense" if dense else "image"
+    dl, sl, hl, hsl = make_operand(P, M, fmt, seed * 2 + 1, dense)
+    dr, sr, hr, hsr = make_operand(P, N, fmt, seed * 2 + 2, dense)
+    if scale_patch is not None:
+        scale_patch(sl, hsl, sr, hsr)
+    out = mxq.scaled_matmul(dl, sl, dr, sr, fmt, res, dense_scale=dense)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = oracle.scaled_matmul(hl, hsl, hr, hsr, fmt, layout=layout)
+    L = values64(hl, hsl, P, M, fmt, layout)
+    R = values64(hr, hsr, P, N, fmt, layout)
+    compare(got, ref, bound(L, R, res, ref, adds_per_block))
     return got, ref
 
 
@@ -119,12 +142,101 @@ def test_matmul_empty_k_is_zero():
     assert bool((out == 0).all())
 
 
-def test_matmul_e8m0_255_is_nan():
-    def patch(sl, hsl):
-        sl[0, 1] = 255            # logical row group 0 (image row 0), column 1 of lhs
-        hsl[0, 1] = 255
-    got, ref = check(32, 8, 8, "e4m3fn", torch.float32, seed=9, scale_patch=patch)
-    assert np.isnan(got[1]).all() and not np.isnan(np.delete(got, 1, axis=0)).any()
+def _patch_255(lhs_blocks=(), rhs_blocks=(), small=60):
+    """Scale patch: E8M0 255 on the given (row group, column) blocks of lhs
+    and rhs; the other operand's row groups that meet them get E8M0 `small`
+    so that the products stay inside fp32."""
+    def patch(sl, hsl, sr, hsr):
+        for g, c in lhs_blocks:
+            slot = (g % 4) + 32 * (g // 4)
+            for t, h in ((sl, hsl), (sr, hsr)):
+                t[slot, :] = small
+                h[slot, :] = small
+            sl[slot, c] = 255
+            hsl[slot, c] = 255
+        for g, c in rhs_blocks:
+            slot = (g % 4) + 32 * (g // 4)
+            if not any(g == gl for gl, _ in lhs_blocks):
+                sl[slot, :] = small
+                hsl[slot, :] = small
+            sr[slot, c] = 255
+            hsr[slot, c] = 255
+    return patch
+
+
+@pytest.mark.parametrize("res", [torch.float32, torch.bfloat16])
+def test_matmul_e8m0_255_lhs_block(res):
+    """An E8M0 of 255 is the scale 2^128 (the consumer's ldexpf), not NaN."""
+    got, ref = check(32, 72, 136, "e4m3fn", res, seed=9, scale_patch=_patch_255(lhs_blocks=[(1, 2), (3, 70)]),
+                     adds_per_block=4)
+    assert np.isfinite(got).all() and np.abs(got[2]).max() > 2.0 ** 60
+
+
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2"])
+def test_matmul_e8m0_255_rhs_block(fmt):
+    got, ref = check(40, 64, 260, fmt, torch.float32, seed=10,
+                     scale_patch=_patch_255(rhs_blocks=[(0, 0), (4, 259), (2, 100)]), adds_per_block=4)
+    assert np.isfinite(got).all() and np.abs(got[:, 259]).max() > 2.0 ** 60
+
+
+def test_matmul_e8m0_255_both_sides():
+    """255 on both sides of one block pair: 2^256 times a nonzero block sum
+    is beyond fp32 (infinity of the sum's sign); the rest stays exact."""
+    def patch(sl, hsl, sr, hsr):
+        _patch_255(lhs_blocks=[(2, 5)])(sl, hsl, sr, hsr)
+        sr[2, 6] = 255                  # row group 2 is image row 2
+        hsr[2, 6] = 255
+    got, ref = check(24, 16, 16, "e4m3fn", torch.float32, seed=12, scale_patch=patch, adds_per_block=4)
+    assert np.isinf(got[5, 6])
+
+
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2"])
+def test_matmul_and_dequantize_agree_on_element_values(fmt):
+    """Both consumers give an element the value decode(q) * 2^(E8M0 - 127)
+    under every E8M0 byte: with a one-hot rhs (R[k][n] = 1 if k == n) the
+    GPU matmul returns the lhs elements themselves, and they equal the GPU
+    dequantize's f32 values (infinities included where the value passes
+    the fp32 range)."""
+    P, M = 8, 256                                  # K = 32, one block per column
+    rng = np.random.default_rng(71)
+    nan_code = {"e4m3fn": 0x7E, "e5m2": 0x7B}[fmt]
+    codes = rng.integers(0, 256, size=(P, 4 * M), dtype=np.uint8)
+    codes = np.where((codes & 0x7F) > nan_code, (codes & 0x80) | nan_code, codes).astype(np.uint8)
+    image = np.zeros((P, M), np.uint8)
+    image[0, :] = np.arange(256)                  # every byte once
+    one = {"e4m3fn": 0x38, "e5m2": 0x3C}[fmt]
+    rhs = np.zeros((P, 4 * 32), np.uint8)
+    for k in range(32):
+        rhs[k // 4, 4 * k + k % 4] = one
+    rs = np.zeros((P, 32), np.uint8)
+    rs[0, :] = 127
+    dl, sl = torch.from_numpy(codes).cuda(), torch.from_numpy(image).cuda()
+    dr, sr = torch.from_numpy(rhs).cuda(), torch.from_numpy(rs).cuda()
+    out = mxq.scaled_matmul(dl, sl, dr, sr, fmt, torch.float32)            # [M, K]
+    deq = mxq.dequantize(dl, sl, fmt, torch.float32)                       # [P, 4M]
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().T                                              # [K, M]
+    want = _k_major(deq.cpu().numpy(), P, M)
+    bad = np.argwhere(got != want)
+    if bad.size:
+        k, m = bad[0]
+        raise AssertionError("%d of %d elements differ; first k=%d column %d (E8M0 %d): matmul %r dequantize %r"
+                             % (len(bad), got.size, k, m, image[0, m], got[k, m], want[k, m]))
+    assert np.isinf(want[:, 255]).any()
+
+
+def test_matmul_bf16_result_is_rounded_f32_result():
+    """The bf16 result is the f32 result rounded to nearest-even, bit for
+    bit: both launches run the same MFMA sequence on the same operands."""
+    P, M, N = 96, 132, 260
+    dl, sl, _, _ = make_operand(P, M, "e4m3fn", 31)
+    dr, sr, _, _ = make_operand(P, N, "e4m3fn", 32)
+    f = mxq.scaled_matmul(dl, sl, dr, sr, "e4m3fn", torch.float32)
+    b = mxq.scaled_matmul(dl, sl, dr, sr, "e4m3fn", torch.bfloat16)
+    torch.cuda.synchronize()
+    want = oracle.f32_to_bf16(f.cpu().numpy())
+    got = b.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    assert np.array_equal(got, want)
 
 
 def test_matmul_full_size_sampled():
@@ -154,9 +266,9 @@ def test_matmul_full_size_sampled():
     ref = oracle.scaled_matmul(np.ascontiguousarray(hl), np.ascontiguousarray(hsl),
                                np.ascontiguousarray(hr), np.ascontiguousarray(hsr), "e4m3fn")
     got = out[torch.from_numpy(ms).cuda()][:, torch.from_numpy(ns).cuda()].cpu().numpy().astype(np.float64)
-    L = _k_major(oracle.dequantize(hl, hsl, P, 4 * 32, "e4m3fn", "f32").astype(np.float64), P, 32)
-    R = _k_major(oracle.dequantize(hr, hsr, P, 4 * 32, "e4m3fn", "f32").astype(np.float64), P, 32)
-    tol = bound(L, R, torch.float32)
+    L = values64(hl, hsl, P, 32, "e4m3fn")
+    R = values64(hr, hsr, P, 32, "e4m3fn")
+    tol = bound(L, R, torch.float32, ref)
     err = np.abs(got - ref)
     progress("full size: relative error median %.3g max %.3g"
              % (np.median(err / np.abs(ref)), (err / np.abs(ref)).max()))
