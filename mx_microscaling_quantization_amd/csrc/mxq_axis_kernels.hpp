@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mxq_quantize_kernels.hpp"
 
 namespace mxq {
@@ -90,40 +92,57 @@ __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__res
         }
     }
 
+    // All 8 view rows' codes, then the rare special-code pass (which lays the
+    // view rows out again from the loaded rows), then the 8 stores, each
+    // with its own data and address registers: a store waiting on write
+    // backpressure then holds up nothing after it.
     const uint64_t F = 4 * N;
-#pragma unroll
-    for (int pr = 0; pr < 8; pr++) {
-        const uint64_t p = (uint64_t)band * 8u + pr;
-        // the view row's input dwords, laid out as the plain quantize holds a
-        // strip row: block b's elements j = 0..3 in w[2b] (j = 0, 1), w[2b+1]
-        uint32_t w[2 * NB];
+    constexpr int OW = OUT == kOutE2M1 ? NW : NB;   // output words per view row
+    // view row pr's input dwords, laid out as the plain quantize holds a
+    // strip row: block b's elements j = 0..3 in w[2b] (j = 0, 1), w[2b+1]
+    auto view_row = [&](int pr, uint32_t *w) {
 #pragma unroll
         for (int b = 0; b < NB; b++) {
             const int h = b / 2, q = b & 1;
             w[2 * b] = half16(v[4 * pr][h], q) | half16(v[4 * pr + 1][h], q) << 16;
             w[2 * b + 1] = half16(v[4 * pr + 2][h], q) | half16(v[4 * pr + 3][h], q) << 16;
         }
+    };
+    uint32_t out[8][OW];
+#pragma unroll
+    for (int pr = 0; pr < 8; pr++) {
+        uint32_t w[2 * NB];
+        view_row(pr, w);
         if constexpr (OUT == kOutE2M1) {
-            uint32_t out[NW];
 #pragma unroll
             for (int h = 0; h < NW; h++) {
-                out[h] = fp4_container<IN, 0>(0u, w[4 * h], w[4 * h + 1], s[2 * h]);
+                out[pr][h] = fp4_container<IN, 0>(0u, w[4 * h], w[4 * h + 1], s[2 * h]);
                 if constexpr (NB > 1)
-                    out[h] = fp4_container<IN, 1>(out[h], w[4 * h + 2], w[4 * h + 3], s[2 * h + 1]);
+                    out[pr][h] = fp4_container<IN, 1>(out[pr][h], w[4 * h + 2], w[4 * h + 3], s[2 * h + 1]);
             }
-            if (special)
-                fix_special_codes<IN, OUT, NB>(w, e, out);
-            store_bytes<2 * NB, 1>(data + (p * F) / 2 + 2 * n0, out);
         } else {
-            uint32_t out[NB];
 #pragma unroll
             for (int b = 0; b < NB; b++)
-                out[b] = fp8x4<IN, OUT>(w[2 * b], w[2 * b + 1], s[b]);
-            if (special)
-                fix_special_codes<IN, OUT, NB>(w, e, out);
-            store_bytes<4 * NB, 1>(data + p * F + 4 * n0, out);
+                out[pr][b] = fp8x4<IN, OUT>(w[2 * b], w[2 * b + 1], s[b]);
         }
     }
+    if (special) {
+#pragma unroll
+        for (int pr = 0; pr < 8; pr++) {
+            uint32_t w[2 * NB];
+            view_row(pr, w);
+            fix_special_codes<IN, OUT, NB>(w, e, out[pr]);
+        }
+    }
+    uint8_t *dst[8];
+#pragma unroll
+    for (int pr = 0; pr < 8; pr++) {
+        const uint64_t p = (uint64_t)band * 8u + pr;
+        dst[pr] = OUT == kOutE2M1 ? data + (p * F) / 2 + 2 * n0 : data + p * F + 4 * n0;
+    }
+#pragma unroll
+    for (int pr = 0; pr < 8; pr++)
+        store_bytes<OUT == kOutE2M1 ? 2 * NB : 4 * NB, 1>(dst[pr], out[pr]);
 
     const uint64_t slot = dense ? (uint64_t)band : (uint64_t)(band & 3u) + 32u * (uint64_t)(band >> 2);
     uint32_t packed[1] = {0};
@@ -199,13 +218,17 @@ __global__ __launch_bounds__(64 * kAlongWaves) void quantize_along_kernel(const 
     const uint64_t G = K / 32;
     const uint64_t g = (uint64_t)tk * 2u + bl;
 
+    // Every load is issued, back to back: a lane past the tensor reads the
+    // first row of block column 0 (in bounds) and zeroes what it got. (With
+    // the loads behind per-row branches, the compiler waited for the second
+    // load to land before issuing the other fourteen.)
     u32x4_t v[4 * KG];
 #pragma unroll
     for (uint32_t k = 0; k < 4 * KG; k++) {
         const uint64_t m = m0 + kAlongWaveRows * w + 4u * i + (k & 3u) + 32u * (k >> 2);
-        v[k] = u32x4_t{0u, 0u, 0u, 0u};
-        if (g < G && m < M)
-            v[k] = load<1>(reinterpret_cast<const u32x4_t *>(in + m * K + g * 32u + 8u * q));
+        const bool ok = g < G && m < M;
+        v[k] = load<1>(reinterpret_cast<const u32x4_t *>(in + (ok ? m * K + g * 32u : 0u) + 8u * q));
+        v[k] = ok ? v[k] : u32x4_t{0u, 0u, 0u, 0u};
     }
 
 #pragma unroll
@@ -254,31 +277,35 @@ __global__ __launch_bounds__(64 * kAlongWaves) void quantize_along_kernel(const 
     const uint64_t F = 4 * M;
     constexpr uint32_t RPL = NARROW ? 1 : 4;     // rows per lane and store
     constexpr uint32_t VPW = 16 / kAlongWaves;   // view rows per wave
+    constexpr uint32_t SPR = RT / (64 * RPL);    // stores per view row and lane
+    // the store's type: RPL rows of CB code bytes
+    using T = typename std::conditional<NARROW, typename std::conditional<OUT == kOutE2M1, uint16_t, uint32_t>::type,
+                                        typename std::conditional<OUT == kOutE2M1, u32x2_t, u32x4_t>::type>::type;
+    // All of the wave's LDS reads first, then its stores, each with its own
+    // data and address registers: a store waiting on write backpressure then
+    // holds up nothing after it.
+    T val[VPW][SPR];
+    uint8_t *dst[VPW][SPR];
+    bool ok[VPW][SPR];
 #pragma unroll
     for (uint32_t j = 0; j < VPW; j++) {
         const uint32_t vr = VPW * w + j;
         const uint64_t gg = (uint64_t)tk * 2u + (vr >> 3);
         const uint64_t p = gg * 8u + (vr & 7u);
 #pragma unroll
-        for (uint32_t s = 0; s < RT / (64 * RPL); s++) {
+        for (uint32_t s = 0; s < SPR; s++) {
             const uint32_t r = 64u * RPL * s + RPL * l;
-            if (gg < G && m0 + r < M) {
-                const uint8_t *src = codes + vr * PITCH + CB * r;
-                uint8_t *dst = OUT == kOutE2M1 ? data + (p * F) / 2 + 2u * (m0 + r) : data + p * F + 4u * (m0 + r);
-                if constexpr (NARROW) {
-                    if constexpr (OUT == kOutE2M1)
-                        store<1>(reinterpret_cast<uint16_t *>(dst), *reinterpret_cast<const uint16_t *>(src));
-                    else
-                        store<1>(reinterpret_cast<uint32_t *>(dst), *reinterpret_cast<const uint32_t *>(src));
-                } else {
-                    if constexpr (OUT == kOutE2M1)
-                        store<1>(reinterpret_cast<u32x2_t *>(dst), *reinterpret_cast<const u32x2_t *>(src));
-                    else
-                        store<1>(reinterpret_cast<u32x4_t *>(dst), *reinterpret_cast<const u32x4_t *>(src));
-                }
-            }
+            ok[j][s] = gg < G && m0 + r < M;
+            val[j][s] = *reinterpret_cast<const T *>(codes + vr * PITCH + CB * r);
+            dst[j][s] = OUT == kOutE2M1 ? data + (p * F) / 2 + 2u * (m0 + r) : data + p * F + 4u * (m0 + r);
         }
     }
+#pragma unroll
+    for (uint32_t j = 0; j < VPW; j++)
+#pragma unroll
+        for (uint32_t s = 0; s < SPR; s++)
+            if (ok[j][s])
+                store<1>(reinterpret_cast<T *>(dst[j][s]), val[j][s]);
     // the two scale strips: the E8M0 of block gg for rows m0 .. m0 + RT - 1
     // goes to the placed (or dense) row of gg at column m
 #pragma unroll

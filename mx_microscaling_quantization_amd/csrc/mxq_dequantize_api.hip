@@ -97,12 +97,22 @@ int mxq_dequantize_ex(const void *data, const void *scale_in, int64_t P, int64_t
     uint32_t a5 = (uint32_t)tiles_per_group;
     uint32_t a6 = (flags & MXQ_FLAG_DENSE_SCALE) ? 1u : 0u;
     void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5, &a6};
-    // at most 8 waves per CU once the tensor outgrows the cache (measured on
-    // the 1.07 G-element e4m3fn -> bf16 decode: 529 us uncapped, 486 us);
-    // one-block FP4 -> bf16 strips (F % 8 == 4) move the fewest bytes per
-    // thread and keep more in flight at 12 (131072 x 8188: 581 us at 8, 521
-    // us at 12; the other one-block paths are as fast or faster at 8)
-    const uint32_t waves = (nb == 1 && fmt == MXQ_OUT_E2M1 && res_dtype == MXQ_RES_BF16) ? 12u : 8u;
+    // A residency cap once the tensor outgrows the cache, set per path by a
+    // sweep at 131072 x 8192 (waves per CU 6, 8, 10, 12, 16, uncapped):
+    //   e4m3fn -> f32   6: 824-832 us, 8: 844-855 us, uncapped 904 us
+    //   e2m1 -> f32     8: 708 us, 10: 741 us, 6: 853 us
+    //   e4m3fn -> bf16  6: 472-474 us, 8: 478-479 us, uncapped 513 us
+    //   e2m1 -> bf16    16: 417 us, 12: 435 us, 8: 470 us
+    // One-block strips (F % 8 == 4) keep their earlier sweep: 8 waves, 12
+    // for FP4 -> bf16, which moves the fewest bytes per thread (131072 x
+    // 8188: 581 us at 8, 521 us at 12).
+    uint32_t waves;
+    if (res_dtype == MXQ_RES_F32)
+        waves = fmt == MXQ_OUT_E2M1 ? 8u : 6u;
+    else if (nb == 2)
+        waves = fmt == MXQ_OUT_E2M1 ? 16u : 6u;
+    else
+        waves = fmt == MXQ_OUT_E2M1 ? 12u : 8u;
     const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, res_dtype == MXQ_RES_F32 ? 5 : 3, kThreads, waves);
     hipError_t err = hipLaunchKernel((const void *)k, dim3((uint32_t)(groups * tiles_per_group)), dim3(kThreads),
                                      args, lds, (hipStream_t)stream);
