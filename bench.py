@@ -150,7 +150,7 @@ def make_input(workload: str, device):
 
     spec = workloads.WORKLOADS[workload]
     P, F = spec["P"], spec["F"]
-    if workload == "bf16-131072x8192-colscaled":
+    if workload in workloads.DEVICE_DRAWN:
         xt = workloads.colscaled_bf16_device(P, F, seed=spec["seed"], device=str(device))
     else:
         x = workloads.make_host(workload)

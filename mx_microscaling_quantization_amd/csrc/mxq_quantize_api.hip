@@ -23,9 +23,9 @@ using mxq_host::grid_fits;
 // bytes, so 12 waves keep as much in flight (131072 x 8188: -> e4m3fn 549 us
 // at 10, 535 us at 12; -> e2m1 529 us at 8, 437 us at 12).
 constexpr uint32_t kThreads = 64;
-inline uint32_t waves_per_cu(int out_dtype, int nb)
+inline uint32_t waves_per_cu(int out_dtype, int nb, bool own)
 {
-    if (nb == 1)
+    if (nb == 1 || own)
         return 12u;
     return out_dtype == MXQ_OUT_E2M1 ? 8u : 10u;
 }
@@ -38,10 +38,24 @@ inline uint32_t waves_per_cu(int out_dtype, int nb)
 // contiguous range of tiles keeps both halves of almost every shared line
 // in one L2 (F = 8200: 729 -> 538 us; F = 8188: 944 -> 582 us; aligned
 // pitches measured faster without it).
+//
+// FP8 output with two-block strips on such a pitch goes further: each
+// one-wave workgroup owns 48 strips, also quantizes the next 16, and writes
+// exactly the 128-byte lines that start inside its own strips, so that every
+// line but the one a row boundary splits is written whole by one wave. The
+// extra strips cost a third more loads (L2 hits: the neighbour reads them
+// too) and pay off at 12 waves per CU (131072 rows, -> e4m3fn: F = 8200
+// 553 -> 527 us; F = 8208 538 -> 523 us; the aligned F = 8192 takes 476 us).
+// Narrower strips (one block, or FP4's 4 bytes a row) would need a second
+// workgroup's worth of extra strips; they keep the shared lines.
 constexpr int kXcds = 8;
 inline bool pitch_aligned(int64_t F, int out_dtype)
 {
     return (out_dtype == MXQ_OUT_E2M1 ? F / 2 : F) % 128 == 0;
+}
+inline bool owns_lines(bool aligned, int out_dtype, int nb)
+{
+    return !aligned && out_dtype != MXQ_OUT_E2M1 && nb == 2;
 }
 
 typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, uint32_t, int,
@@ -52,18 +66,22 @@ typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint
 constexpr int kGroupsPerThread = 1;
 constexpr int kNonTemporal = 3;
 
-template <int IN, int OUT, int XCD> kernel_fn pick_nb(int nb)
+template <int IN, int OUT, int XCD> kernel_fn pick_nb(int nb, bool own)
 {
+    if constexpr (OUT != mxq::kOutE2M1 && XCD != 0) {
+        if (own)
+            return (kernel_fn)mxq::quantize_kernel<IN, OUT, 2, kGroupsPerThread, kNonTemporal, XCD, 1>;
+    }
     return nb == 2 ? (kernel_fn)mxq::quantize_kernel<IN, OUT, 2, kGroupsPerThread, kNonTemporal, XCD>
                    : (kernel_fn)mxq::quantize_kernel<IN, OUT, 1, kGroupsPerThread, kNonTemporal, XCD>;
 }
 
-template <int IN, int XCD> kernel_fn pick_out(int out_dtype, int nb)
+template <int IN, int XCD> kernel_fn pick_out(int out_dtype, int nb, bool own)
 {
     switch (out_dtype) {
-    case MXQ_OUT_E4M3FN: return pick_nb<IN, mxq::kOutE4M3FN, XCD>(nb);
-    case MXQ_OUT_E5M2: return pick_nb<IN, mxq::kOutE5M2, XCD>(nb);
-    default: return pick_nb<IN, mxq::kOutE2M1, XCD>(nb);
+    case MXQ_OUT_E4M3FN: return pick_nb<IN, mxq::kOutE4M3FN, XCD>(nb, own);
+    case MXQ_OUT_E5M2: return pick_nb<IN, mxq::kOutE5M2, XCD>(nb, own);
+    default: return pick_nb<IN, mxq::kOutE2M1, XCD>(nb, own);
     }
 }
 
@@ -99,17 +117,21 @@ int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_
     const int nb = (F % 8 == 0) ? 2 : 1;
     const int64_t nstrips = F / (4 * nb);
     const uint32_t threads = kThreads;
-    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, waves_per_cu(out_dtype, nb));
     const bool aligned = pitch_aligned(F, out_dtype);
-    const int64_t tiles_per_band = (nstrips + threads - 1) / threads;
+    const bool own = owns_lines(aligned, out_dtype, nb);
+    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, waves_per_cu(out_dtype, nb, own));
+    const int64_t per_tile = own ? threads - mxq::kOwnExtra : threads;
+    const int64_t tiles_per_band = (nstrips + per_tile - 1) / per_tile;
     const int64_t groups = P / 8;
     const int64_t bands = (groups + kGroupsPerThread - 1) / kGroupsPerThread;
     if (!grid_fits(bands, tiles_per_band, threads))
         return MXQ_E_OVERFLOW;
 
     kernel_fn k = in_dtype == MXQ_IN_BF16
-                      ? (aligned ? pick_out<mxq::kInBF16, 0>(out_dtype, nb) : pick_out<mxq::kInBF16, kXcds>(out_dtype, nb))
-                      : (aligned ? pick_out<mxq::kInF16, 0>(out_dtype, nb) : pick_out<mxq::kInF16, kXcds>(out_dtype, nb));
+                      ? (aligned ? pick_out<mxq::kInBF16, 0>(out_dtype, nb, false)
+                                 : pick_out<mxq::kInBF16, kXcds>(out_dtype, nb, own))
+                      : (aligned ? pick_out<mxq::kInF16, 0>(out_dtype, nb, false)
+                                 : pick_out<mxq::kInF16, kXcds>(out_dtype, nb, own));
     const uint16_t *a0 = (const uint16_t *)in;
     uint8_t *a1 = (uint8_t *)data_out;
     uint8_t *a2 = (uint8_t *)scale_out;

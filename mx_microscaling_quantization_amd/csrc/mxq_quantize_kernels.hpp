@@ -261,7 +261,17 @@ template <int XCD> __device__ __forceinline__ uint32_t tile_index()
 //   emax_bias  EMAX of the output format, or EMAX - 1 (alternative mode)
 //   dense      0: scale row of group i is (i mod 4) + 32*floor(i/4) of the
 //              P-row image; 1: row i of a dense [P/8, F/4] array
-template <int IN, int OUT, int NB, int GPT, int NT, int XCD = 0>
+//
+// OWN != 0 (FP8 codes, NB = 2; for row pitches that are not a multiple of
+// 128 bytes): each workgroup owns blockDim.x - kOwnExtra strips and also
+// computes the next kOwnExtra (the next workgroup's first ones), and in
+// every row it writes exactly the 128-byte lines that start inside its own
+// strips -- so no line is written in part by two workgroups (except the one
+// a row boundary splits). 16 strips of 8 bytes reach past any line boundary
+// within 128 bytes.
+constexpr uint32_t kOwnExtra = 16;
+
+template <int IN, int OUT, int NB, int GPT, int NT, int XCD = 0, int OWN = 0>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ in,
                                                        uint8_t *__restrict__ data,
                                                        uint8_t *__restrict__ scale,
@@ -270,10 +280,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
                                                        int emax_bias, uint32_t dense)
 {
     static_assert(NB == 1 || NB == 2 || NB == 4, "a strip is 1, 2 or 4 blocks");
+    static_assert(!OWN || (NB == 2 && GPT == 1 && OUT != kOutE2M1), "line ownership: FP8, two-block strips");
     constexpr int LD = NT & 1, ST = (NT >> 1) & 1;
     const uint32_t tile = tile_index<XCD>();
     const uint32_t band = tile / tiles_per_band;
-    const uint32_t strip = (tile - band * tiles_per_band) * blockDim.x + threadIdx.x;
+    const uint32_t run = tile - band * tiles_per_band;
+    const uint32_t owned = OWN ? blockDim.x - kOwnExtra : blockDim.x;
+    const uint32_t strip = run * owned + threadIdx.x;
     if (strip >= nstrips)
         return;
 
@@ -337,6 +350,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
                     out[b] = fp8x4<IN, OUT>(w[j][r][2 * b], w[j][r][2 * b + 1], s[b]);
                 if (special)
                     fix_special_codes<IN, OUT, NB>(w[j][r], e, out);
+                if constexpr (OWN) {
+                    // this row's lines from the first one starting at or
+                    // after the run's first byte, to the first one starting
+                    // at or after the next run's (the row's own ends at
+                    // either side); both neighbours place the boundary at
+                    // the same address
+                    const uint64_t base = (uint64_t)(uintptr_t)data + row * F;
+                    const uint64_t c0 = 8ull * owned * run, c1 = c0 + 8ull * owned;
+                    const uint64_t lo = run == 0 ? 0 : ((base + c0 + 127) & ~127ull) - base;
+                    const uint64_t hi = run + 1 == tiles_per_band ? F : ((base + c1 + 127) & ~127ull) - base;
+                    const uint64_t c = 8ull * strip;
+                    if (c < lo || c >= hi)
+                        continue;
+                }
                 store_bytes<4 * NB, ST>(data + row * F + (uint64_t)strip * (4 * NB), out);
             }
         }
@@ -344,6 +371,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
         // Scale placement: logical row `group` goes to image row
         // (group mod 4) + 32 * floor(group / 4), or to row `group` of the
         // dense array.
+        if (OWN && threadIdx.x >= owned)
+            continue; // the next run's strips: their scales are that run's
         const uint64_t slot = dense ? (uint64_t)group : (uint64_t)(group & 3u) + 32u * (uint64_t)(group >> 2);
         uint32_t packed[1] = {0};
 #pragma unroll

@@ -167,32 +167,29 @@ def test_workload_bf16_16384x8192_blockexp():
     check_against_oracle(workloads.blockexp_bf16(), "bf16", "e2m1", "bf16-16384x8192-blockexp")
 
 
-def test_workload_bf16_131072x8192_colscaled():
-    """Full size, same call as the bench; every data byte and every scale
-    image row (placed rows against the oracle, unplaced rows against their
-    sentinel) is compared with the oracle, run over whole 32-row bands on
-    the host's threads."""
+def _whole_tensor_check(xt: torch.Tensor, out: str, tag: str) -> np.ndarray:
+    """Quantize a large bf16 device tensor in one call and compare every data
+    byte and every scale image row (placed rows against the oracle, unplaced
+    rows against their sentinel) with the oracle, run over whole 32-row bands
+    on the host's threads. Returns the GPU's scale image."""
     from bands import run_bands
 
-    P, F = 131072, 8192
-    progress("bf16-131072x8192-colscaled: generate on device")
-    xt = workloads.colscaled_bf16_device(P, F, seed=5)
-    progress("bf16-131072x8192-colscaled: quantize")
-    data = torch.empty((P, F), dtype=torch.uint8, device="cuda")
+    P, F = xt.shape
+    progress("%s: quantize" % tag)
+    data = torch.empty(mxq.data_shape(P, F, out), dtype=torch.uint8, device="cuda")
     image = torch.full((P, F // 4), SENTINEL, dtype=torch.uint8, device="cuda")
-    mxq.quantize(xt, "e4m3fn", data_out=data, scale_out=image)
+    mxq.quantize(xt, out, data_out=data, scale_out=image)
     torch.cuda.synchronize()
-    progress("bf16-131072x8192-colscaled: copy to host")
+    progress("%s: copy to host" % tag)
     x = xt.view(torch.int16).cpu().numpy().view(np.uint16)
-    del xt
     d_gpu, im_gpu = data.cpu().numpy(), image.cpu().numpy()
     del data, image
-    oracle.quantize(np.zeros((8, 4), np.uint16), "bf16", "e4m3fn")     # load the library before the threads
-    progress("bf16-131072x8192-colscaled: whole-tensor oracle compare")
+    oracle.quantize(np.zeros((8, 4), np.uint16), "bf16", out)     # load the library before the threads
+    progress("%s: whole-tensor oracle compare" % tag)
 
     def check(r0, r1):
         fill = np.full((r1 - r0, F // 4), SENTINEL, np.uint8)
-        d_ref, im_ref = oracle.quantize(x[r0:r1], "bf16", "e4m3fn", image=fill)
+        d_ref, im_ref = oracle.quantize(x[r0:r1], "bf16", out, image=fill)
         if not np.array_equal(d_gpu[r0:r1], d_ref):
             r, c = np.argwhere(d_gpu[r0:r1] != d_ref)[0]
             return "data differs at (%d, %d): gpu %#x oracle %#x" % (r0 + r, c, d_gpu[r0 + r, c], d_ref[r, c])
@@ -202,10 +199,75 @@ def test_workload_bf16_131072x8192_colscaled():
         return None
 
     bad = run_bands(P, check)
-    assert not bad, "%d slabs differ; first: %s" % (len(bad), bad[0])
+    assert not bad, "%s: %d slabs differ; first: %s" % (tag, len(bad), bad[0])
+    return im_gpu
+
+
+def test_workload_bf16_131072x8192_colscaled():
+    """Full size, same call as the bench, every output byte compared."""
+    P, F = 131072, 8192
+    progress("bf16-131072x8192-colscaled: generate on device")
+    xt = workloads.colscaled_bf16_device(P, F, seed=5)
+    im_gpu = _whole_tensor_check(xt, "e4m3fn", "bf16-131072x8192-colscaled")
     # the input is finite: every placed scale is in range
     placed = im_gpu.reshape(P // 32, 32, F // 4)[:, :4, :]
     assert int(placed.min()) >= 1 and int(placed.max()) <= 254 - 8
+
+
+# ------------------------------------------------------ misaligned row pitches
+
+# FP8 codes on a pitch of F % 8 == 0, F % 128 != 0 bytes: each workgroup owns
+# 48 two-block strips (384 bytes a row), also quantizes the next 16, and
+# writes the 128-byte lines that start inside its own strips. These pitches
+# put the run boundaries at many offsets within a line, and include one strip
+# past a run (49 strips), a run ending at the row's end, several runs per
+# row, and a single short run.
+OWN_SHAPES = [(72, 392), (24, 776), (16, 8200), (8, 8208), (40, 3080), (32, 1160), (8, 120), (264, 1544)]
+
+
+@pytest.mark.parametrize("in_dtype,out", COMBOS)
+@pytest.mark.parametrize("P,F", OWN_SHAPES)
+def test_misaligned_pitch_line_ownership(in_dtype, out, P, F):
+    x = workloads.random_bits(P, F, in_dtype, seed=P * 131 + F, specials=True)
+    check_against_oracle(x, in_dtype, out, "own-lines")
+
+
+@pytest.mark.parametrize("offset", (16, 48, 112))
+@pytest.mark.parametrize("out", ("e4m3fn", "e2m1"))
+def test_output_pointers_off_a_line(out, offset):
+    """Data and scale buffers that start `offset` bytes into a 128-byte line:
+    the line ownership follows the absolute addresses; nothing is written
+    before or after either buffer."""
+    P, F = 64, 1032
+    x = workloads.random_bits(P, F, "bf16", seed=offset, specials=True)
+    xt = to_device(x, "bf16")
+    nbytes = mxq.data_bytes(P, F, out)
+    buf = torch.full((offset + nbytes + GUARD,), 0xEE, dtype=torch.uint8, device="cuda")
+    data = buf[offset:offset + nbytes].view(mxq.data_shape(P, F, out))
+    sbytes = P * (F // 4)
+    sbuf = torch.full((offset + sbytes + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda")
+    image = sbuf[offset:offset + sbytes].view(P, F // 4)
+    progress("pointer offset %d bf16->%s %dx%d" % (offset, out, P, F))
+    mxq.quantize(xt, out, data_out=data, scale_out=image)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    sb = sbuf.cpu().numpy()
+    assert np.all(b[:offset] == 0xEE) and np.all(b[offset + nbytes:] == 0xEE)
+    assert np.all(sb[:offset] == SENTINEL) and np.all(sb[offset + sbytes:] == SENTINEL)
+    fill = np.full((P, F // 4), SENTINEL, np.uint8)
+    d_ref, im_ref = oracle.quantize(x, "bf16", out, image=fill)
+    assert np.array_equal(b[offset:offset + nbytes].reshape(d_ref.shape), d_ref)
+    assert np.array_equal(sb[offset:offset + sbytes].reshape(P, F // 4), im_ref)
+
+
+@pytest.mark.parametrize("F,out", [(8200, "e4m3fn"), (8208, "e5m2"), (8188, "e4m3fn"), (8200, "e2m1")])
+def test_misaligned_pitch_16384_rows_whole(F, out):
+    """16384 rows on misaligned pitches (line-owning FP8 path; one-block
+    strips at F % 8 == 4; FP4), every output byte compared."""
+    P = 16384
+    progress("bf16-%dx%d: generate on device" % (P, F))
+    xt = workloads.colscaled_bf16_device(P, F, seed=F)
+    _whole_tensor_check(xt, out, "bf16-%dx%d->%s" % (P, F, out))
 
 
 # --------------------------------------------------------------- other checks

@@ -18,6 +18,9 @@ Workloads (P x F, input type, output types, seed, value recipe):
   x = U(-1, 1) * 2^k. Output e2m1.
 * ``bf16-131072x8192-colscaled`` -- z * c_f, z ~ N(0,1) drawn on the device,
   per-column c_f = exp(N(0, 1)). Output e4m3fn. 1.07 G elements, 2 GiB in.
+* ``bf16-131072x8200-colscaled``, ``bf16-131072x8188-colscaled`` -- the same
+  recipe on row pitches that are not a multiple of 128 bytes (F % 8 == 0 and
+  F % 8 == 4). Outputs e4m3fn and e2m1. Measurement cases for those pitches.
 
 The pages measure on no dataset, so these seeded recipes stand alone.
 """
@@ -31,7 +34,11 @@ WORKLOADS = {
     "f16-8192x14336-student-t": dict(P=8192, F=14336, in_dtype="f16", outs=("e5m2",), seed=3),
     "bf16-16384x8192-blockexp": dict(P=16384, F=8192, in_dtype="bf16", outs=("e2m1",), seed=4),
     "bf16-131072x8192-colscaled": dict(P=131072, F=8192, in_dtype="bf16", outs=("e4m3fn",), seed=5),
+    "bf16-131072x8200-colscaled": dict(P=131072, F=8200, in_dtype="bf16", outs=("e4m3fn", "e2m1"), seed=6),
+    "bf16-131072x8188-colscaled": dict(P=131072, F=8188, in_dtype="bf16", outs=("e4m3fn", "e2m1"), seed=7),
 }
+# Workloads drawn on the device (too large to draw on the host).
+DEVICE_DRAWN = ("bf16-131072x8192-colscaled", "bf16-131072x8200-colscaled", "bf16-131072x8188-colscaled")
 
 # Hand-placed blocks of the 128x512 workload: (row group, column block).
 HANDPLACED = {"zero": (0, 0), "ties": (3, 17), "outlier": (7, 64), "subnormal": (15, 127)}
