@@ -423,9 +423,8 @@ __device__ __attribute__((noinline)) void mm_rare_part(const uint8_t *lhs, const
     mm_epilogue<EPI>(acc, wm0, wn0, M, N, out, out_scale, emax_bias, dense, i, h);
 }
 
-// The kernel.
-
-// results are one aligned 16-byte (f32) or 8-byte (bf16) store.
+// The kernel: one 256 x 256 result tile per workgroup, the main loop in
+// ping-pong, then the finiteness check, then the epilogue.
 template <int FMT, int EPI>
 __global__ __launch_bounds__(kMmThreads) void scaled_matmul_kernel(
     const uint8_t *__restrict__ lhs, const uint8_t *__restrict__ lhs_scale, const uint8_t *__restrict__ rhs,
