@@ -110,13 +110,22 @@ __device__ __forceinline__ void decode_block_e255(uint32_t w, uint32_t *out)
 }
 
 // The dequantize kernel. Grid as the quantize (GPT = 1): one workgroup per
-// (row group, run of blockDim.x strips); XCD != 0 renumbers workgroups as
-// the quantize does, so each XCD walks one contiguous range of tiles.
+// (row group, run of strips); XCD != 0 renumbers workgroups as the quantize
+// does, so each XCD walks one contiguous range of tiles.
 //   data    FP8: P*F bytes; FP4: P*F/2 bytes
 //   scale   the P x F/4 scale image (only the placed rows are read), or with
 //           dense = 1 the [P/8, F/4] scale array
 //   out     P x F results, fp32 or bf16
-template <int FMT, int RES, int NB, int NT, int XCD = 0>
+//
+// OWN != 0 (for result rows that are not a multiple of 128 bytes): a
+// workgroup owns blockDim.x - dq_own_extra(lane bytes) strips and also
+// decodes the next ones, and in every row it writes exactly the 128-byte
+// lines that start inside its own strips, so that no line is written in part
+// by two workgroups (except the one a row boundary splits). 128 bytes of
+// extra strips reach past any line boundary.
+constexpr uint32_t dq_own_extra(uint32_t lane_bytes) { return 128u / lane_bytes; }
+
+template <int FMT, int RES, int NB, int NT, int XCD = 0, int OWN = 0>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restrict__ data,
                                                          const uint8_t *__restrict__ scale,
                                                          void *__restrict__ out, uint64_t F,
@@ -126,9 +135,13 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
     static_assert(NB == 1 || NB == 2, "a strip is 1 or 2 blocks");
     constexpr int LD = NT & 1, ST = (NT >> 1) & 1;
     constexpr int RES_BYTES = RES == kResF32 ? 4 : 2;
+    constexpr uint32_t LANE_BYTES = 4 * NB * RES_BYTES;
+    static_assert(!OWN || LANE_BYTES == 16 || LANE_BYTES == 8, "line ownership: 8 or 16 result bytes per row");
     const uint32_t tile = tile_index<XCD>();
     const uint32_t group = tile / tiles_per_band;
-    const uint32_t strip = (tile - group * tiles_per_band) * blockDim.x + threadIdx.x;
+    const uint32_t run = tile - group * tiles_per_band;
+    const uint32_t owned = OWN ? blockDim.x - dq_own_extra(LANE_BYTES) : blockDim.x;
+    const uint32_t strip = run * owned + threadIdx.x;
     if (strip >= nstrips)
         return;
 
@@ -155,6 +168,34 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
     // codes of all 8 rows first, then convert and store row by row
     uint32_t c[8][NB];
     const uint64_t row0 = (uint64_t)group * 8u;
+
+    // With OWN, this thread stores the rows whose 16 bytes lie in the lines
+    // from the first one starting at or after the run's first byte to the
+    // first one starting at or after the next run's (the row's own ends at
+    // either side); both neighbours place each boundary at the same address.
+    // Each row is a buffer over that row (row pitch < 2^31 bytes, checked on
+    // the host), and a row this thread does not own gets an offset past the
+    // buffer's end, which the hardware drops: no branch. The offsets are
+    // fixed here, before the loads, in registers of their own: computed
+    // between the stores, they took the registers of the previous store's
+    // data and made each store wait for the one before.
+    __amdgpu_buffer_rsrc_t own_rs[8];
+    uint32_t own_off[8];
+    if constexpr (OWN) {
+        const uint32_t rowbytes = (uint32_t)(F * RES_BYTES);
+        const uint32_t c0 = LANE_BYTES * owned * run, c1 = c0 + LANE_BYTES * owned;
+        const uint32_t c = LANE_BYTES * strip;
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            uint8_t *rowp = reinterpret_cast<uint8_t *>(out) + (row0 + r) * (uint64_t)rowbytes;
+            const uint32_t mis = (uint32_t)(uintptr_t)rowp & 127u; // row start within its line
+            const uint32_t lo = run == 0 ? 0u : ((mis + c0 + 127u) & ~127u) - mis;
+            const uint32_t hi = run + 1 == tiles_per_band ? rowbytes : ((mis + c1 + 127u) & ~127u) - mis;
+            own_rs[r] = __builtin_amdgcn_make_buffer_rsrc(rowp, (short)0, (int)rowbytes, kBufferFlags);
+            own_off[r] = (c >= lo && c < hi) ? c : kDropOffset;
+            asm volatile("" : "+v"(own_off[r]));
+        }
+    }
     // The 8 destinations, each its own address: a single pointer stepped
     // between the stores shared registers with the first store's data, and
     // a store blocked on write backpressure then held up the rest of the
@@ -213,6 +254,19 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t *__restri
                 else
                     decode_block_e255<FMT, RES, 1>(w, res[r] + b * RES_BYTES);
             }
+    }
+    if constexpr (OWN) {
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            if constexpr (LANE_BYTES == 16) {
+                u32x4_t v = {res[r][0], res[r][1], res[r][2], res[r][3]};
+                __builtin_amdgcn_raw_buffer_store_b128(v, own_rs[r], (int)own_off[r], 0, ST ? kBufferNT : 0);
+            } else {
+                u32x2_t v = {res[r][0], res[r][1]};
+                __builtin_amdgcn_raw_buffer_store_b64(v, own_rs[r], (int)own_off[r], 0, ST ? kBufferNT : 0);
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int r = 0; r < 8; r++) {

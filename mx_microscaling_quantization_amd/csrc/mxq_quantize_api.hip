@@ -23,9 +23,9 @@ using mxq_host::grid_fits;
 // bytes, so 12 waves keep as much in flight (131072 x 8188: -> e4m3fn 549 us
 // at 10, 535 us at 12; -> e2m1 529 us at 8, 437 us at 12).
 constexpr uint32_t kThreads = 64;
-inline uint32_t waves_per_cu(int out_dtype, int nb, bool own)
+inline uint32_t waves_per_cu(int out_dtype, int nb)
 {
-    if (nb == 1 || own)
+    if (nb == 1)
         return 12u;
     return out_dtype == MXQ_OUT_E2M1 ? 8u : 10u;
 }
@@ -44,18 +44,20 @@ inline uint32_t waves_per_cu(int out_dtype, int nb, bool own)
 // exactly the 128-byte lines that start inside its own strips, so that every
 // line but the one a row boundary splits is written whole by one wave. The
 // extra strips cost a third more loads (L2 hits: the neighbour reads them
-// too) and pay off at 12 waves per CU (131072 rows, -> e4m3fn: F = 8200
-// 553 -> 527 us; F = 8208 538 -> 523 us; the aligned F = 8192 takes 476 us).
-// Narrower strips (one block, or FP4's 4 bytes a row) would need a second
-// workgroup's worth of extra strips; they keep the shared lines.
+// too). 131072 rows -> e4m3fn, same box, caps 10 / 11 / 12 / 14 waves per
+// CU: F = 8200 525 / 527 / 531 / 545 us (547 us with shared lines); F =
+// 8208 518 / 518 / 522 / 534 us (537 us); the aligned F = 8192 takes 476 us.
+// Narrower strips (one block, or FP4's 4 bytes a row) would need as many
+// extra strips as owned ones; they keep the shared lines.
 constexpr int kXcds = 8;
 inline bool pitch_aligned(int64_t F, int out_dtype)
 {
     return (out_dtype == MXQ_OUT_E2M1 ? F / 2 : F) % 128 == 0;
 }
-inline bool owns_lines(bool aligned, int out_dtype, int nb)
+inline bool owns_lines(bool aligned, int out_dtype, int nb, int64_t F)
 {
-    return !aligned && out_dtype != MXQ_OUT_E2M1 && nb == 2;
+    // rows that one 32-bit buffer range covers with room for the dropped offset
+    return !aligned && out_dtype != MXQ_OUT_E2M1 && nb == 2 && F < (int64_t)mxq::kDropOffset;
 }
 
 typedef void (*kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t, uint32_t, uint32_t, uint32_t, int,
@@ -118,8 +120,8 @@ int mxq_quantize_ex(const void *in, int64_t P, int64_t F, int in_dtype, int out_
     const int64_t nstrips = F / (4 * nb);
     const uint32_t threads = kThreads;
     const bool aligned = pitch_aligned(F, out_dtype);
-    const bool own = owns_lines(aligned, out_dtype, nb);
-    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, waves_per_cu(out_dtype, nb, own));
+    const bool own = owns_lines(aligned, out_dtype, nb, F);
+    const uint32_t lds = mxq_host::occupancy_cap_lds(P * F, 3, threads, waves_per_cu(out_dtype, nb));
     const int64_t per_tile = own ? threads - mxq::kOwnExtra : threads;
     const int64_t tiles_per_band = (nstrips + per_tile - 1) / per_tile;
     const int64_t groups = P / 8;

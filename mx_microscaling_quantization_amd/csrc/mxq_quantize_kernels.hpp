@@ -270,6 +270,12 @@ template <int XCD> __device__ __forceinline__ uint32_t tile_index()
 // a row boundary splits). 16 strips of 8 bytes reach past any line boundary
 // within 128 bytes.
 constexpr uint32_t kOwnExtra = 16;
+// Raw untyped buffer (32-bit data format); the non-temporal cache-policy
+// bit of buffer stores; an offset past any buffer used with it (stores at
+// such an offset are dropped by the buffer's range check).
+constexpr uint32_t kBufferFlags = 0x00020000u;
+constexpr int kBufferNT = 2;
+constexpr uint32_t kDropOffset = 0x80000000u;
 
 template <int IN, int OUT, int NB, int GPT, int NT, int XCD = 0, int OWN = 0>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restrict__ in,
@@ -291,6 +297,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
         return;
 
     const uint32_t g0 = band * GPT;
+
+    // With OWN, this thread stores the rows whose 8 bytes lie in the lines
+    // from the first one starting at or after the run's first byte to the
+    // first one starting at or after the next run's (the row's own ends at
+    // either side); both neighbours place each boundary at the same address.
+    // Each row is a buffer over that row (row pitch < 2^31 bytes, checked on
+    // the host), and a row this thread does not own gets an offset past the
+    // buffer's end, which the hardware drops: no branch around the stores.
+    // The offsets are fixed here, before the loads, in registers of their
+    // own: computed between the stores, they took the registers of the
+    // previous store's data and made each store wait for the one before.
+    __amdgpu_buffer_rsrc_t own_rs[8];
+    uint32_t own_off[8];
+    if constexpr (OWN) {
+        const uint32_t c0 = 8u * owned * run, c1 = c0 + 8u * owned, c = 8u * strip;
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            uint8_t *rowp = data + ((uint64_t)g0 * 8u + r) * F;
+            const uint32_t mis = (uint32_t)(uintptr_t)rowp & 127u; // row start within its line
+            const uint32_t lo = run == 0 ? 0u : ((mis + c0 + 127u) & ~127u) - mis;
+            const uint32_t hi = run + 1 == tiles_per_band ? (uint32_t)F : ((mis + c1 + 127u) & ~127u) - mis;
+            own_rs[r] = __builtin_amdgcn_make_buffer_rsrc(rowp, (short)0, (int)F, kBufferFlags);
+            own_off[r] = (c >= lo && c < hi) ? c : kDropOffset;
+            asm volatile("" : "+v"(own_off[r]));
+        }
+    }
 
     uint32_t w[GPT][8][2 * NB];
 #pragma unroll
@@ -328,6 +360,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
             special |= mag > InfBits<IN>::value || e[b] == 254u;
         }
 
+        uint32_t own_codes[8][NB]; // with OWN: every row's codes, stored after the loop
 #pragma unroll
         for (int r = 0; r < 8; r++) {
             const uint64_t row = row0 + r;
@@ -351,20 +384,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *__restric
                 if (special)
                     fix_special_codes<IN, OUT, NB>(w[j][r], e, out);
                 if constexpr (OWN) {
-                    // this row's lines from the first one starting at or
-                    // after the run's first byte, to the first one starting
-                    // at or after the next run's (the row's own ends at
-                    // either side); both neighbours place the boundary at
-                    // the same address
-                    const uint64_t base = (uint64_t)(uintptr_t)data + row * F;
-                    const uint64_t c0 = 8ull * owned * run, c1 = c0 + 8ull * owned;
-                    const uint64_t lo = run == 0 ? 0 : ((base + c0 + 127) & ~127ull) - base;
-                    const uint64_t hi = run + 1 == tiles_per_band ? F : ((base + c1 + 127) & ~127ull) - base;
-                    const uint64_t c = 8ull * strip;
-                    if (c < lo || c >= hi)
-                        continue;
+#pragma unroll
+                    for (int b = 0; b < NB; b++)
+                        own_codes[r][b] = out[b];
+                } else {
+                    store_bytes<4 * NB, ST>(data + row * F + (uint64_t)strip * (4 * NB), out);
                 }
-                store_bytes<4 * NB, ST>(data + row * F + (uint64_t)strip * (4 * NB), out);
+            }
+        }
+        if constexpr (OWN) {
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                u32x2_t v = {own_codes[r][0], own_codes[r][1]};
+                __builtin_amdgcn_raw_buffer_store_b64(v, own_rs[r], (int)own_off[r], 0, ST ? kBufferNT : 0);
             }
         }
 

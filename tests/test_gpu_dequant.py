@@ -136,3 +136,88 @@ def test_full_size_dequantize():
     bad = run_bands(P, check)
     assert not bad, "%d slabs differ; first: %s" % (len(bad), bad[0])
     assert not ((got & 0x7F80) == 0x7F80).any()                          # no Inf or NaN
+
+
+# ------------------------------------------------------ misaligned result pitches
+
+# Result rows that are not a multiple of 128 bytes, with 16 result bytes per
+# thread and row (bf16 with F % 8 == 0, or f32): each workgroup owns 56
+# strips, also decodes the next 8, and writes the 128-byte lines that start
+# inside its own strips. These shapes put the run boundaries at many offsets
+# within a line, one strip past a run (57 and 58 strips), runs ending at the
+# row's end, several runs per row, and single short runs.
+OWN_SHAPES = [(24, 456), (72, 232), (16, 8200), (8, 8208), (40, 900), (32, 1160), (8, 120), (264, 1544)]
+
+
+@pytest.mark.parametrize("res", list(RES))
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("P,F", OWN_SHAPES)
+def test_misaligned_result_pitch_line_ownership(fmt, res, P, F):
+    progress("dequant own-lines %s->%s %dx%d" % (fmt, res, P, F))
+    rng = np.random.default_rng(P * 31 + F)
+    data = rng.integers(0, 256, size=_data_bytes(P, F, fmt), dtype=np.uint8)
+    image = rng.integers(0, 256, size=(P, F // 4), dtype=np.uint8)
+    image[0] = np.resize(np.array([0, 255, 254, 1, 127], np.uint8), image.shape[1])
+    got = gpu_dequantize(data, image, P, F, fmt, res)
+    ref = oracle.dequantize(data, image, P, F, fmt, res).reshape(P, F)
+    assert_same(got, ref, res, "own-lines")
+
+
+@pytest.mark.parametrize("offset", (16, 48, 112))
+@pytest.mark.parametrize("res", list(RES))
+def test_result_pointer_off_a_line(res, offset):
+    """A result buffer starting `offset` bytes into a 128-byte line: the line
+    ownership follows the absolute addresses; nothing is written before or
+    after the buffer."""
+    P, F = 64, 1032
+    progress("dequant pointer offset %d e4m3fn->%s %dx%d" % (offset, res, P, F))
+    rng = np.random.default_rng(offset)
+    data = rng.integers(0, 256, size=P * F, dtype=np.uint8)
+    image = rng.integers(0, 256, size=(P, F // 4), dtype=np.uint8)
+    d = torch.from_numpy(data.reshape(P, F)).cuda()
+    im = torch.from_numpy(image).cuda()
+    esz = 4 if res == "f32" else 2
+    pad = offset // esz
+    buf = torch.full((pad + P * F + GUARD,), 7.0, dtype=RES[res], device="cuda")
+    out = buf[pad:pad + P * F].view(P, F)
+    mxq.dequantize(d, im, "e4m3fn", RES[res], out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == 7.0).all()) and bool((buf[pad + P * F:] == 7.0).all()), "write outside the buffer"
+    ref = oracle.dequantize(data, image, P, F, "e4m3fn", res).reshape(P, F)
+    assert_same(_np_view(out), ref, res, "pointer offset")
+
+
+@pytest.mark.parametrize("F,fmt,res", [(8200, "e4m3fn", "bf16"), (8200, "e2m1", "f32"), (8200, "e5m2", "f32"),
+                                        (8200, "e2m1", "bf16"), (8188, "e4m3fn", "bf16"), (8188, "e2m1", "bf16")])
+def test_misaligned_16384_rows_whole(F, fmt, res):
+    """16384 rows on the line-owning paths (16 result bytes per thread and
+    row at F = 8200; 8 with the one-block strips of F = 8188 to bf16),
+    quantized on the device from the column-scaled recipe and decoded; every
+    result compared with the oracle over whole 32-row bands on the host's
+    threads."""
+    from bands import run_bands
+
+    P = 16384
+    progress("dequant 16384x%d %s->%s: generate + quantize" % (F, fmt, res))
+    xt = workloads.colscaled_bf16_device(P, F, seed=11)
+    d, im = mxq.quantize(xt, fmt)
+    del xt
+    out = mxq.dequantize(d, im, fmt, RES[res])
+    torch.cuda.synchronize()
+    got = _np_view(out)
+    hd, him = d.cpu().numpy().reshape(-1), im.cpu().numpy()
+    del out, d, im
+    row_bytes = F // 2 if fmt == "e2m1" else F
+    oracle.dequantize(hd[:32 * row_bytes], him[:32], 32, F, fmt, res)     # load the library before the threads
+    progress("dequant 16384x%d %s->%s: whole-tensor oracle compare" % (F, fmt, res))
+
+    def check(r0, r1):
+        ref = oracle.dequantize(hd[r0 * row_bytes:r1 * row_bytes], him[r0:r1], r1 - r0, F, fmt, res).reshape(r1 - r0, F)
+        ref_bits = ref.view(np.uint32) if res == "f32" else ref
+        if not np.array_equal(got[r0:r1], ref_bits):
+            r, c = np.argwhere(got[r0:r1] != ref_bits)[0]
+            return "result differs at (%d, %d): gpu %#x oracle %#x" % (r0 + r, c, got[r0 + r, c], ref_bits[r, c])
+        return None
+
+    bad = run_bands(P, check)
+    assert not bad, "%d slabs differ; first: %s" % (len(bad), bad[0])
