@@ -28,10 +28,21 @@ typedef void (*along_kernel_fn)(const uint16_t *, uint8_t *, uint8_t *, uint64_t
 // tiles of every window of 32 workgroups. 8192 columns, bf16 -> e4m3fn:
 // 131080 rows 621 -> 593 us, 131074 672 -> 631 us, 131040 593 -> 565 us;
 // multiples of 256 rows are as fast or faster without it (131072: 545 us).
+//
+// The down kernel with four-column strips on such a pitch owns its lines, as
+// the plain quantize does: each workgroup quantizes 128 bytes' worth of
+// strips beyond its own and writes exactly the 128-byte lines that start
+// inside its own (W [131072, 8200], bit-identical; two boxes):
+//   -> e4m3fn 568 -> 546 us at 8 waves per CU, 551 -> 524 us at 7 (537 at 6)
+//   -> e2m1   489 -> 477 us at 8, 469 -> 459 us at 8 (482 at 7)
 constexpr int kXcds = 8;
 
-template <int IN, int OUT, int XCD> down_kernel_fn down_pick_nb(int nb)
+template <int IN, int OUT, int XCD> down_kernel_fn down_pick_nb(int nb, bool own)
 {
+    if constexpr (XCD != 0) {
+        if (own && nb == 4)
+            return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 4, XCD, 1>;
+    }
     switch (nb) {
     case 4: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 4, XCD>;
     case 2: return (down_kernel_fn)mxq::quantize_down_kernel<IN, OUT, 2, XCD>;
@@ -39,9 +50,9 @@ template <int IN, int OUT, int XCD> down_kernel_fn down_pick_nb(int nb)
     }
 }
 
-template <int IN, int OUT> down_kernel_fn down_pick(int nb, bool aligned)
+template <int IN, int OUT> down_kernel_fn down_pick(int nb, bool aligned, bool own)
 {
-    return aligned ? down_pick_nb<IN, OUT, 0>(nb) : down_pick_nb<IN, OUT, kXcds>(nb);
+    return aligned ? down_pick_nb<IN, OUT, 0>(nb, false) : down_pick_nb<IN, OUT, kXcds>(nb, own);
 }
 
 template <int IN, int OUT> along_kernel_fn along_pick(int narrow)
@@ -51,19 +62,20 @@ template <int IN, int OUT> along_kernel_fn along_pick(int narrow)
 }
 
 template <int IN>
-void axis_pick(int out_dtype, int down, int width, bool aligned, down_kernel_fn *d, along_kernel_fn *a)
+void axis_pick(int out_dtype, int down, int width, bool aligned, bool own, down_kernel_fn *d,
+               along_kernel_fn *a)
 {
     switch (out_dtype) {
     case MXQ_OUT_E4M3FN:
-        *d = down ? down_pick<IN, mxq::kOutE4M3FN>(width, aligned) : nullptr;
+        *d = down ? down_pick<IN, mxq::kOutE4M3FN>(width, aligned, own) : nullptr;
         *a = down ? nullptr : along_pick<IN, mxq::kOutE4M3FN>(width);
         break;
     case MXQ_OUT_E5M2:
-        *d = down ? down_pick<IN, mxq::kOutE5M2>(width, aligned) : nullptr;
+        *d = down ? down_pick<IN, mxq::kOutE5M2>(width, aligned, own) : nullptr;
         *a = down ? nullptr : along_pick<IN, mxq::kOutE5M2>(width);
         break;
     default:
-        *d = down ? down_pick<IN, mxq::kOutE2M1>(width, aligned) : nullptr;
+        *d = down ? down_pick<IN, mxq::kOutE2M1>(width, aligned, own) : nullptr;
         *a = down ? nullptr : along_pick<IN, mxq::kOutE2M1>(width);
         break;
     }
@@ -109,9 +121,14 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
     const int64_t threads = 64;
     int width;
     int64_t grid, tiles;
+    const bool aligned = (out_dtype == MXQ_OUT_E2M1 ? 2 * O : 4 * O) % 128 == 0; // view row pitch
+    // line ownership (down kernel, four-column strips, misaligned view rows
+    // that one 32-bit buffer range covers with room for the dropped offset)
+    const bool own = down && !aligned && O % 4 == 0 && 4 * O < (int64_t)mxq::kDropOffset;
     if (down) {
         width = (O % 4 == 0) ? 4 : (O % 2 == 0) ? 2 : 1; // columns per thread
-        tiles = (O / width + threads - 1) / threads;     // per 32-row band
+        const int64_t per_tile = own ? threads - 128 / (out_dtype == MXQ_OUT_E2M1 ? 8 : 16) : threads;
+        tiles = (O / width + per_tile - 1) / per_tile;   // per 32-row band
         if (!grid_fits(K / 32, tiles, threads))
             return MXQ_E_OVERFLOW;
         grid = (K / 32) * tiles;
@@ -125,11 +142,10 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
     }
     down_kernel_fn dk = nullptr;
     along_kernel_fn ak = nullptr;
-    const bool aligned = (out_dtype == MXQ_OUT_E2M1 ? 2 * O : 4 * O) % 128 == 0; // view row pitch
     if (in_dtype == MXQ_IN_BF16)
-        axis_pick<mxq::kInBF16>(out_dtype, down, width, aligned, &dk, &ak);
+        axis_pick<mxq::kInBF16>(out_dtype, down, width, aligned, own, &dk, &ak);
     else
-        axis_pick<mxq::kInF16>(out_dtype, down, width, aligned, &dk, &ak);
+        axis_pick<mxq::kInF16>(out_dtype, down, width, aligned, own, &dk, &ak);
 
     const uint16_t *a0 = (const uint16_t *)in;
     uint8_t *a1 = (uint8_t *)data_out;
@@ -147,7 +163,9 @@ int mxq_quantize_axis(const void *in, int64_t R, int64_t C, int in_dtype, int ou
         // 746 us at 8, 665 us at 12; two- and four-column strips are fastest
         // at 8); the along kernel's own LDS tile already sets its residency,
         // and more reserve slows it
-        const uint32_t lds = mxq_host::occupancy_cap_lds(K * O, 3, (uint32_t)threads, width == 1 ? 12 : 8);
+        // (owned lines: 7 for FP8, 8 for FP4, from the sweep above)
+        const uint32_t waves = own ? (out_dtype == MXQ_OUT_E2M1 ? 8u : 7u) : width == 1 ? 12u : 8u;
+        const uint32_t lds = mxq_host::occupancy_cap_lds(K * O, 3, (uint32_t)threads, waves);
         err = hipLaunchKernel((const void *)dk, dim3((uint32_t)grid), dim3((uint32_t)threads), args, lds,
                               (hipStream_t)stream);
     } else {

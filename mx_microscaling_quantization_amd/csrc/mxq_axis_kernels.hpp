@@ -39,10 +39,14 @@ __device__ __forceinline__ uint32_t half16(uint32_t w, uint32_t h) { return (w >
 // the strip is NB containers: 4*NB bytes (FP8) or 2*NB (FP4) at
 // p * 4N + 4*n0 (FP8) / p * 2N + 2*n0 (FP4); the NB E8M0 bytes go to the
 // placed (or dense) scale row at column n0.
-//   nstrips   N / NB;  tiles_per_band  ceil(nstrips / 64); XCD != 0
-//   renumbers workgroups as the plain quantize does (each XCD walks one
-//   contiguous range of tiles)
-template <int IN, int OUT, int NB, int XCD = 0>
+//   nstrips   N / NB;  tiles_per_band  ceil(nstrips / strips per tile);
+//   XCD != 0 renumbers workgroups as the plain quantize does (each XCD walks
+//   one contiguous range of tiles)
+// OWN != 0 (8 or 16 code bytes per thread and view row; for view rows that
+// are not a multiple of 128 bytes): as in the plain quantize, a workgroup
+// owns 64 - 128 / (bytes per thread) strips, also quantizes the next ones,
+// and writes exactly the 128-byte lines that start inside its own strips.
+template <int IN, int OUT, int NB, int XCD = 0, int OWN = 0>
 __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__restrict__ in,
                                                            uint8_t *__restrict__ data,
                                                            uint8_t *__restrict__ scale, uint64_t N,
@@ -51,12 +55,37 @@ __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__res
 {
     static_assert(NB == 1 || NB == 2 || NB == 4, "1, 2 or 4 columns per thread");
     constexpr int NW = (NB + 1) / 2;   // loaded dwords per row
+    constexpr uint32_t LANE_BYTES = OUT == kOutE2M1 ? 2 * NB : 4 * NB; // code bytes per view row
+    static_assert(!OWN || LANE_BYTES >= 8, "line ownership: 8 or 16 code bytes per view row");
     const uint32_t tile = tile_index<XCD>();
     const uint32_t band = tile / tiles_per_band;
-    const uint32_t strip = (tile - band * tiles_per_band) * 64u + threadIdx.x;
+    const uint32_t run = tile - band * tiles_per_band;
+    const uint32_t owned = OWN ? 64u - 128u / LANE_BYTES : 64u;
+    const uint32_t strip = run * owned + threadIdx.x;
     if (strip >= nstrips)
         return;
     const uint64_t n0 = (uint64_t)strip * NB;
+
+    // With OWN: the view rows' buffers and this thread's store offsets (an
+    // offset past the row's range for a row it does not own, which the
+    // hardware drops), fixed before the loads in registers of their own, as
+    // in the plain quantize. View row pitch < 2^31 bytes (checked on the host).
+    __amdgpu_buffer_rsrc_t own_rs[8];
+    uint32_t own_off[8];
+    if constexpr (OWN) {
+        const uint32_t rowbytes = (uint32_t)(OUT == kOutE2M1 ? 2 * N : 4 * N);
+        const uint32_t c0 = LANE_BYTES * owned * run, c1 = c0 + LANE_BYTES * owned, c = LANE_BYTES * strip;
+#pragma unroll
+        for (int pr = 0; pr < 8; pr++) {
+            uint8_t *rowp = data + ((uint64_t)band * 8u + pr) * rowbytes;
+            const uint32_t mis = (uint32_t)(uintptr_t)rowp & 127u; // row start within its line
+            const uint32_t lo = run == 0 ? 0u : ((mis + c0 + 127u) & ~127u) - mis;
+            const uint32_t hi = run + 1 == tiles_per_band ? rowbytes : ((mis + c1 + 127u) & ~127u) - mis;
+            own_rs[pr] = __builtin_amdgcn_make_buffer_rsrc(rowp, (short)0, (int)rowbytes, kBufferFlags);
+            own_off[pr] = (c >= lo && c < hi) ? c : kDropOffset;
+            asm volatile("" : "+v"(own_off[pr]));
+        }
+    }
 
     uint32_t v[32][NW];
     const uint16_t *rows = in + (uint64_t)band * 32u * N + n0;
@@ -134,15 +163,30 @@ __global__ __launch_bounds__(64) void quantize_down_kernel(const uint16_t *__res
             fix_special_codes<IN, OUT, NB>(w, e, out[pr]);
         }
     }
-    uint8_t *dst[8];
+    if constexpr (OWN) {
 #pragma unroll
-    for (int pr = 0; pr < 8; pr++) {
-        const uint64_t p = (uint64_t)band * 8u + pr;
-        dst[pr] = OUT == kOutE2M1 ? data + (p * F) / 2 + 2 * n0 : data + p * F + 4 * n0;
+        for (int pr = 0; pr < 8; pr++) {
+            if constexpr (LANE_BYTES == 16) {
+                u32x4_t w = {out[pr][0], out[pr][1], out[pr][2], out[pr][3]};
+                __builtin_amdgcn_raw_buffer_store_b128(w, own_rs[pr], (int)own_off[pr], 0, kBufferNT);
+            } else {
+                u32x2_t w = {out[pr][0], out[pr][1]};
+                __builtin_amdgcn_raw_buffer_store_b64(w, own_rs[pr], (int)own_off[pr], 0, kBufferNT);
+            }
+        }
+        if (threadIdx.x >= owned)
+            return; // the next run's strips: their scales are that run's
+    } else {
+        uint8_t *dst[8];
+#pragma unroll
+        for (int pr = 0; pr < 8; pr++) {
+            const uint64_t p = (uint64_t)band * 8u + pr;
+            dst[pr] = OUT == kOutE2M1 ? data + (p * F) / 2 + 2 * n0 : data + p * F + 4 * n0;
+        }
+#pragma unroll
+        for (int pr = 0; pr < 8; pr++)
+            store_bytes<LANE_BYTES, 1>(dst[pr], out[pr]);
     }
-#pragma unroll
-    for (int pr = 0; pr < 8; pr++)
-        store_bytes<OUT == kOutE2M1 ? 2 * NB : 4 * NB, 1>(dst[pr], out[pr]);
 
     const uint64_t slot = dense ? (uint64_t)band : (uint64_t)(band & 3u) + 32u * (uint64_t)(band >> 2);
     uint32_t packed[1] = {0};

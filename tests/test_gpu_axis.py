@@ -166,3 +166,79 @@ def test_axis_full_size(dim):
 
     bad = run_bands(K // 4, check)
     assert not bad, "%d slabs differ; first: %s" % (len(bad), bad[0])
+
+
+# ---------------------------------------------- dim -2 on misaligned view rows
+
+# Four-column strips on view rows of 4*C (FP8) or 2*C (FP4) bytes that are not
+# a multiple of 128: each workgroup owns 56 (FP8) or 48 (FP4) strips, also
+# quantizes the next 128 bytes' worth, and writes the lines that start inside
+# its own strips. These put run boundaries at many offsets within a line,
+# one or two strips past a run, and several runs per view row.
+OWN_SHAPES = [(32, 232), (64, 196), (32, 452), (96, 900), (64, 8200), (32, 1000)]
+
+
+@pytest.mark.parametrize("in_dtype,fmt", [("bf16", "e4m3fn"), ("bf16", "e5m2"), ("bf16", "e2m1"),
+                                          ("f16", "e4m3fn"), ("f16", "e2m1")])
+@pytest.mark.parametrize("R,C", OWN_SHAPES)
+def test_axis_down_line_ownership(R, C, in_dtype, fmt):
+    progress("quantize_axis own-lines dim=-2 %dx%d %s->%s" % (R, C, in_dtype, fmt))
+    bits = workloads.random_bits(R, C, in_dtype, seed=R * 5 + C, specials=True)
+    run(bits, in_dtype, fmt, -2)
+
+
+@pytest.mark.parametrize("offset", (16, 48, 112))
+@pytest.mark.parametrize("fmt", ("e4m3fn", "e2m1"))
+def test_axis_down_pointer_off_a_line(fmt, offset):
+    """A data buffer starting `offset` bytes into a 128-byte line: the line
+    ownership follows the absolute addresses; nothing is written before or
+    after the buffer."""
+    R, C = 64, 1000
+    bits = workloads.random_bits(R, C, "bf16", seed=offset, specials=True)
+    P, F = mxq.axis_view_shape(R, C, -2)
+    nd = int(np.prod(mxq.data_shape(P, F, fmt)))
+    buf = torch.full((offset + nd + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda")
+    scale = torch.full(mxq.scale_image_shape(P, F), SENTINEL, dtype=torch.uint8, device="cuda")
+    progress("quantize_axis dim=-2 pointer offset %d %dx%d -> %s" % (offset, R, C, fmt))
+    mxq.quantize_axis(_device(bits, "bf16"), fmt, -2, data_out=buf[offset:offset + nd], scale_out=scale)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert (got[:offset] == SENTINEL).all() and (got[offset + nd:] == SENTINEL).all(), "write outside the buffer"
+    ref_d, _ = oracle.quantize_axis(bits, "bf16", fmt, -2)
+    assert np.array_equal(got[offset:offset + nd].reshape(ref_d.shape), ref_d)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e2m1"])
+def test_axis_down_16384x8200_whole(fmt):
+    """W [16384, 8200] down its columns (misaligned view rows, the owning
+    path): every data byte and placed scale row against the oracle's
+    quantize_axis over slabs of whole 128-row stretches on the host's
+    threads."""
+    from bands import run_bands
+
+    R, C = 16384, 8200
+    progress("quantize_axis dim=-2 %dx%d -> %s: input" % (R, C, fmt))
+    x = workloads.colscaled_bf16_device(R, C, seed=13)
+    d, s = mxq.quantize_axis(x, fmt, -2)
+    torch.cuda.synchronize()
+    bits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    del x
+    hd, hs = d.cpu().numpy(), s.cpu().numpy()
+    del d, s
+    P = hs.shape[0]
+    placed = (np.arange(P // 8) % 4) + 32 * (np.arange(P // 8) // 4)
+    oracle.quantize_axis(bits[:32, :32].copy(), "bf16", fmt, -2)   # load the library before the threads
+    progress("quantize_axis dim=-2 %dx%d -> %s: whole-tensor oracle compare" % (R, C, fmt))
+
+    def check(v0, v1):
+        ref_d, ref_s = oracle.quantize_axis(bits[4 * v0:4 * v1], "bf16", fmt, -2)
+        if not np.array_equal(hd[v0:v1], ref_d):
+            r, c = np.argwhere(hd[v0:v1] != ref_d)[0]
+            return "data differs at view (%d, %d)" % (v0 + r, c)
+        rows = placed[placed < v1 - v0]
+        if not np.array_equal(hs[v0 + rows], ref_s[rows]):
+            return "scale rows differ in view rows [%d, %d)" % (v0, v1)
+        return None
+
+    bad = run_bands(R // 4, check)
+    assert not bad, "%d slabs differ; first: %s" % (len(bad), bad[0])
