@@ -203,8 +203,8 @@ def test_matmul_quantize_e8m0_255_blocks(out_dtype):
 
 def test_matmul_quantize_full_size_sampled():
     """The bench's 8192 x 8192 x 8192 e4m3fn -> e4m3fn case: all bytes
-    against the unfused pair, and 16 sampled blocks (8 rows x 4 columns)
-    against the oracle's exact sums."""
+    against the unfused pair, and 512 sampled blocks (8 rows x 4 columns)
+    against the oracle's exact sums, on the host's threads."""
     P, M, N = 2048, 8192, 8192
     progress("matmul_quantize full size: operands")
     g = torch.Generator(device="cuda")
@@ -221,22 +221,31 @@ def test_matmul_quantize_full_size_sampled():
     torch.cuda.synchronize()
     assert torch.equal(data, ud) and torch.equal(scale, us)
     del ud, us
-    progress("matmul_quantize full size: sampled oracle blocks")
+    progress("matmul_quantize full size: 512 sampled oracle blocks")
+    import concurrent.futures
+    import os
+
     rng = np.random.default_rng(9)
-    for _ in range(16):
-        gi, cb = int(rng.integers(M // 8)), int(rng.integers(N // 4))
+    picks = [(int(rng.integers(M // 8)), int(rng.integers(N // 4))) for _ in range(512)]
+    cols = lambda idx: np.concatenate([np.arange(4 * c, 4 * c + 4) for c in idx])
+    hdata, hscale = data.cpu().numpy(), scale.cpu().numpy()
+    blocks = []
+    for gi, cb in picks:
         ms, ns = np.arange(8 * gi, 8 * gi + 8), np.arange(4 * cb, 4 * cb + 4)
-        cols = lambda idx: np.concatenate([np.arange(4 * c, 4 * c + 4) for c in idx])
-        hl = np.ascontiguousarray(dl[:, torch.from_numpy(cols(ms)).cuda()].cpu().numpy())
-        hr = np.ascontiguousarray(dr[:, torch.from_numpy(cols(ns)).cuda()].cpu().numpy())
-        hsl = np.ascontiguousarray(sl[:, torch.from_numpy(ms).cuda()].cpu().numpy())
-        hsr = np.ascontiguousarray(sr[:, torch.from_numpy(ns).cuda()].cpu().numpy())
+        blocks.append((gi, cb, np.ascontiguousarray(dl[:, torch.from_numpy(cols(ms)).cuda()].cpu().numpy()),
+                       np.ascontiguousarray(sl[:, torch.from_numpy(ms).cuda()].cpu().numpy()),
+                       np.ascontiguousarray(dr[:, torch.from_numpy(cols(ns)).cuda()].cpu().numpy()),
+                       np.ascontiguousarray(sr[:, torch.from_numpy(ns).cuda()].cpu().numpy())))
+
+    def check_block(b):
+        gi, cb, hl, hsl, hr, hsr = b
         exact = oracle.scaled_matmul(hl, hsl, hr, hsr, "e4m3fn")
-        L = values64(hl, hsl, P, 8, "e4m3fn")
-        R = values64(hr, hsr, P, 4, "e4m3fn")
-        tol = bound(L, R, torch.float32, exact)
-        blk_data = data[8 * gi:8 * gi + 8, 4 * cb:4 * cb + 4].cpu().numpy()
-        slot = int(defcheck.scale_slot(gi))
+        tol = bound(values64(hl, hsl, P, 8, "e4m3fn"), values64(hr, hsr, P, 4, "e4m3fn"), torch.float32, exact)
+        blk_data = hdata[8 * gi:8 * gi + 8, 4 * cb:4 * cb + 4]
         blk_scale = np.zeros((8, 1), np.uint8)
-        blk_scale[defcheck.scale_slot(0)] = scale[slot, cb].item()
+        blk_scale[defcheck.scale_slot(0)] = hscale[int(defcheck.scale_slot(gi)), cb]
         check_admissible(exact, tol, blk_data, blk_scale, 8, 4, "e4m3fn", False, "image")
+
+    check_block(blocks[0])   # loads the oracle before the threads
+    with concurrent.futures.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(check_block, blocks[1:]))
