@@ -99,3 +99,50 @@ def test_graph_capture_every_entry_point():
             rows = torch.tensor([(i % 4) + 32 * (i // 4) for i in range(P // 8)], device="cuda")
             assert torch.equal(bufs[k][rows], ref[k][rows]), "replay %d: %s" % (rep, k)
         _ = (X.float() * 2).sum().item()
+
+
+def test_graph_capture_line_owning_launches():
+    """The line-owning launches on row pitches that are not a multiple of
+    128 bytes (FP8 quantize, dequantize to bf16 and f32, quantize down the
+    columns): captured in one graph, every replay equal to the eager
+    results."""
+    g_ = torch.Generator(device="cuda")
+    g_.manual_seed(12)
+    P, F = 512, 8200
+    x = torch.randn((P, F), generator=g_, device="cuda").to(torch.bfloat16)
+    W = torch.randn((256, 1000), generator=g_, device="cuda").to(torch.bfloat16)
+    data = torch.zeros((P, F), dtype=torch.uint8, device="cuda")
+    image = torch.zeros((P, F // 4), dtype=torch.uint8, device="cuda")
+    bf = torch.zeros((P, F), dtype=torch.bfloat16, device="cuda")
+    f32 = torch.zeros((P, F), dtype=torch.float32, device="cuda")
+    VP, VF = mxq.axis_view_shape(256, 1000, -2)
+    wd = torch.zeros(mxq.data_shape(VP, VF, "e4m3fn"), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(mxq.scale_image_shape(VP, VF), dtype=torch.uint8, device="cuda")
+
+    def calls():
+        mxq.quantize(x, "e4m3fn", data_out=data, scale_out=image)
+        mxq.dequantize(data, image, "e4m3fn", torch.bfloat16, out=bf)
+        mxq.dequantize(data, image, "e4m3fn", torch.float32, out=f32)
+        mxq.quantize_axis(W, "e4m3fn", -2, data_out=wd, scale_out=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (data, image, bf, f32, wd, ws)]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(4):
+        for t in (data, bf, f32, wd):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("data", "image", "bf16", "f32", "axis data", "axis scale"),
+                                   (data, image, bf, f32, wd, ws), ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), "replay %d: %s" % (rep, name)
+        _ = (x.float() * 2).sum().item()
