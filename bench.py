@@ -56,6 +56,9 @@ flushes between them. The default, ``hot``,
 runs the launches back to back on the same buffers: a workload under the
 cache size is then served largely from the cache.
 
+The streaming ops' lines also carry ``copy_reference``: a plain 1 GiB device
+copy timed after the measured steps, and the line's value over its rate.
+
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
 WRITE_SIZE readings into bytes. ``--floors`` times plain linear read, write
@@ -436,6 +439,23 @@ def copy_calibration(steps: int, warmup: int) -> None:
                       "copy_GBps": round(4 * n / ms / 1e6, 1)}), flush=True)
 
 
+def copy_reference(stream, steps: int = 20, warmup: int = 3) -> dict:
+    """A plain device-to-device copy of 1 GiB (torch's copy kernel: 1 GiB
+    read, 1 GiB written) timed on the same box right after the measured
+    op, so its line can be read against the copy rate as well as against
+    the 8 TB/s peak. Its buffers are allocated and freed here, outside any
+    timed region of the op."""
+    import torch
+
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    total_ms, avg_ms = _time_steps(lambda: dst.copy_(src), steps, warmup, stream)
+    nbytes = 2 << 30
+    del src, dst
+    return {"kernel": "torch copy_ (device to device), 1 GiB read + 1 GiB written", "bytes_per_copy": nbytes,
+            "us_per_copy": round(avg_ms * 1e3, 2), "GBps": round(nbytes / (avg_ms * 1e-3) / 1e9, 1)}
+
+
 def floors(steps: int, warmup: int) -> None:
     """Plain linear streams with torch's own kernels, for comparison with
     the library's kernels: a read of 2 GiB (a sum), writes of 1 GiB and
@@ -589,6 +609,9 @@ def main() -> int:
                      "traffic_source": traffic_source, "kernel_avg_us": round(avg_launch_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
+    ref = copy_reference(stream)
+    ref["value_over_copy"] = round(value / ref["GBps"], 4)
+    result["copy_reference"] = ref
     if not args.no_cpu_baseline:
         if args.op == "quantize":
             result["cpu_baseline"] = cpu_baseline(xt, out, spec["in_dtype"])
