@@ -56,8 +56,10 @@ flushes between them. The default, ``hot``,
 runs the launches back to back on the same buffers: a workload under the
 cache size is then served largely from the cache.
 
-The streaming ops' lines also carry ``copy_reference``: a plain 1 GiB device
-copy timed after the measured steps, and the line's value over its rate.
+The streaming ops' lines also carry ``per_call`` (the median and minimum of
+20 more calls, each between its own event pair) and ``copy_reference``: a
+plain 1 GiB device copy timed after the measured steps, and the line's value
+over its rate.
 
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
@@ -439,6 +441,28 @@ def copy_calibration(steps: int, warmup: int) -> None:
                       "copy_GBps": round(4 * n / ms / 1e6, 1)}), flush=True)
 
 
+def launch_stats(step, stream, n: int = 20, pre=None) -> dict:
+    """`n` more calls, each between its own pair of HIP events (with `pre`,
+    e.g. a cache flush, before each and outside its events), after the timed
+    region: the median and minimum per call. An event pair around one launch
+    also holds the launch's dispatch, so at small sizes these sit above the
+    back-to-back average."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for k in range(n):
+        if pre is not None:
+            pre()
+        starts[k].record(stream)
+        step()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(starts[k].elapsed_time(ends[k]) * 1e3 for k in range(n))
+    return {"n": n, "median_us": round(us[n // 2], 3), "min_us": round(us[0], 3),
+            "timing": "one event pair per call, after the timed region"}
+
+
 def copy_reference(stream, steps: int = 20, warmup: int = 3) -> dict:
     """A plain device-to-device copy of 1 GiB (torch's copy kernel: 1 GiB
     read, 1 GiB written) timed on the same box right after the measured
@@ -609,6 +633,7 @@ def main() -> int:
                      "traffic_source": traffic_source, "kernel_avg_us": round(avg_launch_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
+    result["per_call"] = launch_stats(step, stream, pre=flush)
     ref = copy_reference(stream)
     ref["value_over_copy"] = round(value / ref["GBps"], 4)
     result["copy_reference"] = ref

@@ -52,6 +52,8 @@ def test_quantize_line_with_cpu_baselines():
     assert d["config"]["bytes_per_step"] == 4096 * 4096 * 2 + 4096 * 4096 + 4096 * 4096 // 32
     # steps run back to back, one launch per step: value equals the roofline's achieved rate
     assert abs(d["value"] - d["roofline"]["achieved"]) <= 0.01 * d["value"]
+    pc = d["per_call"]
+    assert pc["n"] == 20 and 0 < pc["min_us"] <= pc["median_us"]
     ref = d["copy_reference"]
     assert ref["GBps"] > 0 and abs(ref["value_over_copy"] - d["value"] / ref["GBps"]) < 1e-3
     for key in ("cpu_baseline", "cpu_baseline_all_cores"):
