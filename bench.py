@@ -415,6 +415,7 @@ def bench_matmul(args) -> int:
     }
     if compare:
         result["compare"] = compare
+    result["env"] = run_env(args.op)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_matmul(dl, sl, dr, sr, fmt, quantize_out=qout if fused else None)
     print(json.dumps(result), flush=True)
@@ -439,6 +440,17 @@ def copy_calibration(steps: int, warmup: int) -> None:
     ms = s.elapsed_time(e) / steps
     print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "ms_per_copy": round(ms, 4),
                       "copy_GBps": round(4 * n / ms / 1e6, 1)}), flush=True)
+
+
+def run_env(op: str) -> dict:
+    """Where the line was measured: HIP and torch versions, the device and
+    its gfx architecture, and the digest of the op's kernel sources (the
+    same digest that gates the committed traffic summaries)."""
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    return {"hip": torch.version.hip, "torch": torch.__version__, "device": props.name,
+            "gfx_arch": getattr(props, "gcnArchName", None), "kernel_source_sha256_16": kernel_source_digest(op)}
 
 
 def launch_stats(step, stream, n: int = 20, pre=None) -> dict:
@@ -633,6 +645,7 @@ def main() -> int:
                      "traffic_source": traffic_source, "kernel_avg_us": round(avg_launch_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
+    result["env"] = run_env(args.op)
     result["per_call"] = launch_stats(step, stream, pre=flush)
     ref = copy_reference(stream)
     ref["value_over_copy"] = round(value / ref["GBps"], 4)

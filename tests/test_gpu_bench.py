@@ -39,6 +39,8 @@ def _check_common(d, steps, warmup):
     assert roof["peak"] > 0 and roof["achieved"] > 0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert 0 < roof["frac"] < 1.2
+    env = d["env"]
+    assert env["hip"] and env["device"] and env["kernel_source_sha256_16"]
     src = roof["traffic_source"]
     assert "--pmc" in src["kind"] and src["kernel_source_sha256_16"]
     assert (roof["traffic"] is None) or src["matches_current_sources"]
