@@ -376,3 +376,28 @@ def test_concurrent_host_threads():
             P = inputs[k][0].shape[0]
             placed = (np.arange(P // 8) % 4) + 32 * (np.arange(P // 8) // 4)
             assert np.array_equal(im[placed], serial[k][1][placed])
+
+
+@pytest.mark.parametrize("F,out", [(4096, "e4m3fn"), (4104, "e5m2"), (4100, "e2m1"), (8200, "e4m3fn")])
+def test_grid_shape_invariance(F, out):
+    """The same rows give the same bytes whatever grid covers them: the whole
+    tensor in one call against slabs of whole 32-row bands in separate calls
+    (each a different grid), with dense scales so the slabs' scale rows are
+    the whole tensor's rows; the dequantize likewise. Ten repeats of the whole
+    call are identical."""
+    P = 1024
+    x = workloads.random_bits(P, F, "bf16", seed=F, specials=True)
+    xt = to_device(x, "bf16")
+    d_all, s_all = mxq.quantize(xt, out, dense_scale=True)
+    r_all = mxq.dequantize(d_all, s_all, out, torch.float32, dense_scale=True)
+    torch.cuda.synchronize()
+    for _ in range(9):
+        d2, s2 = mxq.quantize(xt, out, dense_scale=True)
+        assert torch.equal(d2, d_all) and torch.equal(s2, s_all)
+    for r0, r1 in ((0, 32), (32, 288), (288, 800), (800, 1024)):
+        d, s = mxq.quantize(xt[r0:r1].contiguous(), out, dense_scale=True)
+        r = mxq.dequantize(d, s, out, torch.float32, dense_scale=True)
+        torch.cuda.synchronize()
+        assert torch.equal(d, d_all[r0:r1]), "data rows [%d, %d)" % (r0, r1)
+        assert torch.equal(s, s_all[r0 // 8:r1 // 8]), "scale rows [%d, %d)" % (r0 // 8, r1 // 8)
+        assert torch.equal(r.view(torch.int32), r_all[r0:r1].view(torch.int32)), "dequantized rows"
