@@ -20,9 +20,11 @@ SENTINEL = 0xA5
 GUARD = 256
 
 # (P, F): 1 row group x 2^22 + 4 columns (1-block strips, misaligned
-# pitch), 1 row group x 2^23 columns (aligned), 2^21 rows x 4 columns (one
-# strip per row group), 2^20 rows x 12 columns (three strips)
-QUANT_SHAPES = [(8, (1 << 22) + 4), (8, 1 << 23), (1 << 21, 4), (1 << 20, 12)]
+# pitch), 1 row group x 2^22 + 8 columns (2-block strips on a misaligned
+# pitch: the line-owning launch for FP8, 10923 runs per row), 1 row group x
+# 2^23 columns (aligned), 2^21 rows x 4 columns (one strip per row group),
+# 2^20 rows x 12 columns (three strips)
+QUANT_SHAPES = [(8, (1 << 22) + 4), (8, (1 << 22) + 8), (8, 1 << 23), (1 << 21, 4), (1 << 20, 12)]
 
 
 def _device(bits: np.ndarray, in_dtype: str) -> torch.Tensor:
@@ -49,26 +51,35 @@ def test_quantize_extreme_shapes(P, F, out):
     assert np.array_equal(image.cpu().numpy(), im_ref)
 
 
-@pytest.mark.parametrize("P,F", [(8, (1 << 22) + 4), (1 << 21, 4)])
-def test_dequantize_extreme_shapes(P, F):
-    progress("dequantize extreme %dx%d" % (P, F))
+# result rows on misaligned pitches take the line-owning launches (16-byte
+# lanes for f32 and for bf16 with F % 8 == 0, 8-byte lanes for bf16 with
+# F % 8 == 4)
+@pytest.mark.parametrize("res", ["f32", "bf16"])
+@pytest.mark.parametrize("P,F", [(8, (1 << 22) + 4), (8, (1 << 22) + 8), (1 << 21, 4), (1 << 20, 12)])
+def test_dequantize_extreme_shapes(P, F, res):
+    progress("dequantize extreme %dx%d -> %s" % (P, F, res))
     x = workloads.random_bits(P, F, "f16", seed=3 * P + F, specials=False)
     d_ref, im_ref = oracle.quantize(x, "f16", "e5m2")
     d = torch.from_numpy(d_ref).cuda()
     im = torch.from_numpy(im_ref).cuda()
-    buf = torch.full((P * F + GUARD,), 7.0, dtype=torch.float32, device="cuda")
+    tdt = torch.float32 if res == "f32" else torch.bfloat16
+    buf = torch.full((P * F + GUARD,), 7.0, dtype=tdt, device="cuda")
     out = buf[:P * F].view(P, F)
-    mxq.dequantize(d, im, "e5m2", torch.float32, out=out)
+    mxq.dequantize(d, im, "e5m2", tdt, out=out)
     torch.cuda.synchronize()
     assert bool((buf[P * F:] == 7.0).all())
-    ref = oracle.dequantize(d_ref, im_ref, P, F, "e5m2", "f32")
-    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    ref = oracle.dequantize(d_ref, im_ref, P, F, "e5m2", res)
+    if res == "f32":
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    else:
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), ref)
 
 
 # (dim, R, C): blocks along rows of a 4-row tensor 2^20 wide, along rows of
 # 2^21 + 4 rows one block wide (the row count not a multiple of 4 -> 3),
 # down the columns of a 32-row band 2^21 wide, down 2^20 rows 4 wide
-AXIS_SHAPES = [(-1, 4, 1 << 20), (-1, (1 << 21) + 3, 32), (-2, 32, 1 << 21), (-2, 1 << 20, 4)]
+AXIS_SHAPES = [(-1, 4, 1 << 20), (-1, (1 << 21) + 3, 32), (-2, 32, 1 << 21), (-2, 1 << 20, 4),
+               (-2, 32, (1 << 21) + 4)]   # the last: misaligned view rows, line-owning four-column strips
 
 
 @pytest.mark.parametrize("dim,R,C", AXIS_SHAPES)
