@@ -10,6 +10,7 @@ raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 
@@ -50,6 +51,8 @@ def library_path() -> str:
 def load():
     """Load ``libmxq.so`` (once) and declare its signatures."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -112,6 +115,41 @@ def _out_code(out_dtype: str) -> int:
         return OUT_DTYPES[out_dtype]
     except KeyError:
         raise MXQError(2, "output element type must be one of %s" % sorted(OUT_DTYPES)) from None
+
+
+# torch's accessor for the raw handle of a device's current stream (what its
+# own kernels launch on), when it has one; the public route costs more per
+# call
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(stream, device: torch.device) -> int:
+    """The raw HIP stream handle to enqueue on: ``stream``'s, else the current
+    stream of ``device``."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_current_stream is not None:
+        return _raw_current_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _call_on(device: torch.device, fn, *args) -> int:
+    """Call ``fn(*args)`` with ``device`` current (the library launches on
+    the current device), entering a device context only when it is not."""
+    if torch.cuda.current_device() == device.index:
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
+
+
+@functools.lru_cache(maxsize=256)
+def _data_nbytes(P: int, F: int, code: int) -> int:
+    return int(load().mxq_data_bytes(P, F, code))
+
+
+@functools.lru_cache(maxsize=256)
+def _scale_nbytes(P: int, F: int, flags: int) -> int:
+    return int(load().mxq_scale_bytes(P, F, flags))
 
 
 def _check_out_buffer(name: str, t: torch.Tensor, nbytes: int, device: torch.device) -> None:
@@ -182,17 +220,15 @@ def quantize(x: torch.Tensor, out_dtype: str = "e4m3fn", data_out: torch.Tensor 
     flags = (FLAG_ALT_EMAX if alt_emax else 0) | (FLAG_DENSE_SCALE if dense_scale else 0)
     if scale_out is None:
         scale_out = torch.empty(scale_image_shape(P, F, dense_scale), dtype=torch.uint8, device=x.device)
-    _check_out_buffer("data_out", data_out, lib.mxq_data_bytes(P, F, code), x.device)
-    _check_out_buffer("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags), x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
-    with torch.cuda.device(x.device):
-        if flags == 0:    # the contract's own entry point
-            _check(lib.mxq_quantize(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, data_out.data_ptr(),
-                                    scale_out.data_ptr(), stream.cuda_stream))
-        else:
-            _check(lib.mxq_quantize_ex(x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, flags, data_out.data_ptr(),
-                                       scale_out.data_ptr(), stream.cuda_stream))
+    _check_out_buffer("data_out", data_out, _data_nbytes(P, F, code), x.device)
+    _check_out_buffer("scale_out", scale_out, _scale_nbytes(P, F, flags), x.device)
+    sh = _stream_handle(stream, x.device)
+    if flags == 0:    # the contract's own entry point
+        _check(_call_on(x.device, lib.mxq_quantize, x.data_ptr(), P, F, IN_DTYPES[x.dtype], code,
+                        data_out.data_ptr(), scale_out.data_ptr(), sh))
+    else:
+        _check(_call_on(x.device, lib.mxq_quantize_ex, x.data_ptr(), P, F, IN_DTYPES[x.dtype], code, flags,
+                        data_out.data_ptr(), scale_out.data_ptr(), sh))
     return data_out, scale_out
 
 
@@ -229,11 +265,9 @@ def dequantize(data: torch.Tensor, scale_image: torch.Tensor, out_dtype: str = "
         out = torch.empty((P, F), dtype=res_dtype, device=data.device)
     elif out.dtype != res_dtype or tuple(out.shape) != (P, F) or not out.is_contiguous() or out.device != data.device:
         raise ValueError("out must be a contiguous [%d, %d] %s tensor on %s" % (P, F, res_dtype, data.device))
-    if stream is None:
-        stream = torch.cuda.current_stream(data.device)
-    with torch.cuda.device(data.device):
-        _check(lib.mxq_dequantize_ex(data.data_ptr(), scale_image.data_ptr(), P, F, code, RES_DTYPES[res_dtype],
-                                     FLAG_DENSE_SCALE if dense_scale else 0, out.data_ptr(), stream.cuda_stream))
+    sh = _stream_handle(stream, data.device)
+    _check(_call_on(data.device, lib.mxq_dequantize_ex, data.data_ptr(), scale_image.data_ptr(), P, F, code,
+                    RES_DTYPES[res_dtype], FLAG_DENSE_SCALE if dense_scale else 0, out.data_ptr(), sh))
     return out
 
 
@@ -272,12 +306,10 @@ def scaled_matmul(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torch.Tensor,
         out = torch.empty((M, N), dtype=res_dtype, device=lhs.device)
     elif out.dtype != res_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous() or out.device != lhs.device:
         raise ValueError("out must be a contiguous [%d, %d] %s tensor on %s" % (M, N, res_dtype, lhs.device))
-    if stream is None:
-        stream = torch.cuda.current_stream(lhs.device)
-    with torch.cuda.device(lhs.device):
-        _check(lib.mxq_scaled_matmul(lhs.data_ptr(), lhs_scale.data_ptr(), rhs.data_ptr(), rhs_scale.data_ptr(), P, M, N,
-                                     code, RES_DTYPES[res_dtype], FLAG_DENSE_SCALE if dense_scale else 0,
-                                     out.data_ptr(), stream.cuda_stream))
+    sh = _stream_handle(stream, lhs.device)
+    _check(_call_on(lhs.device, lib.mxq_scaled_matmul, lhs.data_ptr(), lhs_scale.data_ptr(), rhs.data_ptr(),
+                    rhs_scale.data_ptr(), P, M, N, code, RES_DTYPES[res_dtype],
+                    FLAG_DENSE_SCALE if dense_scale else 0, out.data_ptr(), sh))
     return out
 
 
@@ -304,14 +336,12 @@ def scaled_matmul_quantize(lhs: torch.Tensor, lhs_scale: torch.Tensor, rhs: torc
         data_out = torch.empty(data_shape(M, N, out_dtype), dtype=torch.uint8, device=lhs.device)
     if scale_out is None:
         scale_out = torch.empty(scale_image_shape(M, N, dense_scale), dtype=torch.uint8, device=lhs.device)
-    _check_out_buffer("data_out", data_out, lib.mxq_data_bytes(M, N, out_code), lhs.device)
-    _check_out_buffer("scale_out", scale_out, lib.mxq_scale_bytes(M, N, flags), lhs.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(lhs.device)
-    with torch.cuda.device(lhs.device):
-        _check(lib.mxq_scaled_matmul_quantize(lhs.data_ptr(), lhs_scale.data_ptr(), rhs.data_ptr(),
-                                              rhs_scale.data_ptr(), P, M, N, code, out_code, flags,
-                                              data_out.data_ptr(), scale_out.data_ptr(), stream.cuda_stream))
+    _check_out_buffer("data_out", data_out, _data_nbytes(M, N, out_code), lhs.device)
+    _check_out_buffer("scale_out", scale_out, _scale_nbytes(M, N, flags), lhs.device)
+    sh = _stream_handle(stream, lhs.device)
+    _check(_call_on(lhs.device, lib.mxq_scaled_matmul_quantize, lhs.data_ptr(), lhs_scale.data_ptr(),
+                    rhs.data_ptr(), rhs_scale.data_ptr(), P, M, N, code, out_code, flags,
+                    data_out.data_ptr(), scale_out.data_ptr(), sh))
     return data_out, scale_out
 
 
@@ -349,11 +379,9 @@ def quantize_axis(x: torch.Tensor, out_dtype: str = "e4m3fn", dim: int = -1, dat
         data_out = torch.empty(data_shape(P, F, out_dtype), dtype=torch.uint8, device=x.device)
     if scale_out is None:
         scale_out = torch.empty(scale_image_shape(P, F, dense_scale), dtype=torch.uint8, device=x.device)
-    _check_out_buffer("data_out", data_out, lib.mxq_data_bytes(P, F, code), x.device)
-    _check_out_buffer("scale_out", scale_out, lib.mxq_scale_bytes(P, F, flags), x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
-    with torch.cuda.device(x.device):
-        _check(lib.mxq_quantize_axis(x.data_ptr(), R, C, IN_DTYPES[x.dtype], code, dim, flags, data_out.data_ptr(),
-                                     scale_out.data_ptr(), stream.cuda_stream))
+    _check_out_buffer("data_out", data_out, _data_nbytes(P, F, code), x.device)
+    _check_out_buffer("scale_out", scale_out, _scale_nbytes(P, F, flags), x.device)
+    sh = _stream_handle(stream, x.device)
+    _check(_call_on(x.device, lib.mxq_quantize_axis, x.data_ptr(), R, C, IN_DTYPES[x.dtype], code, dim, flags,
+                    data_out.data_ptr(), scale_out.data_ptr(), sh))
     return data_out, scale_out
