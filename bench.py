@@ -64,7 +64,9 @@ over its rate.
 ``--copy-calibration`` instead times a plain device copy of 2 GiB (read 2 GiB,
 write 2 GiB); its hardware counters give the factor that turns FETCH_SIZE /
 WRITE_SIZE readings into bytes. ``--floors`` times plain linear read, write
-and copy streams (torch's own kernels) for comparison.
+and copy streams (torch's own kernels) for comparison. ``--vendor-gemm`` times
+the vendor's per-tensor-scaled FP8 product at the ``--mm`` sizes, for context
+beside the block-scaled matmul.
 """
 from __future__ import annotations
 
@@ -514,6 +516,30 @@ def floors(steps: int, warmup: int) -> None:
     print(json.dumps({"floors": out, "steps": steps, "warmup": warmup}), flush=True)
 
 
+def vendor_gemm(args) -> None:
+    """Context only, not the library: the vendor's per-tensor-scaled FP8
+    product (torch._scaled_mm, e4m3fn operands, one fp32 scale each, bf16
+    result) at the --mm sizes, timed like the matmul ops (warm-up launches,
+    then `steps` back-to-back launches between two events). It does no
+    per-block scale work, so it bounds what a block-scaled product of the
+    same sizes could reach on this device."""
+    import torch
+
+    M, N, K = args.mm
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    a = (torch.randn(M, K, device="cuda", generator=gen) * 0.5).to(torch.float8_e4m3fn)
+    b = (torch.randn(N, K, device="cuda", generator=gen) * 0.5).to(torch.float8_e4m3fn).t()   # K x N, column-major
+    one = torch.ones((), device="cuda")
+    stream = torch.cuda.current_stream()
+    total_ms, avg_ms = _time_steps(lambda: torch._scaled_mm(a, b, one, one, out_dtype=torch.bfloat16),
+                                   args.steps, args.warmup, stream)
+    flops = 2.0 * M * N * K
+    print(json.dumps({"vendor_gemm": {"op": "torch._scaled_mm, per-tensor e4m3fn, bf16 result", "M": M, "N": N,
+                                      "K": K, "us_per_call": round(avg_ms * 1e3, 2),
+                                      "TFLOPs": round(flops / (avg_ms * 1e-3) / 1e12, 1)},
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,13 +561,15 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--floors", action="store_true",
                     help="time plain linear read / write / copy streams (torch kernels) instead")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor's per-tensor FP8 product at the --mm sizes instead (context only)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU only; --gpus %d is not supported "
               "(rows shard with no exchange, see the design notes)" % args.gpus, file=sys.stderr)
         return 2
-    args.warmup = default_warmup(args.op, args.warmup)
+    args.warmup = default_warmup("matmul" if args.vendor_gemm else args.op, args.warmup)
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
@@ -558,6 +586,9 @@ def main() -> int:
         return 0
     if args.floors:
         floors(args.steps, args.warmup)
+        return 0
+    if args.vendor_gemm:
+        vendor_gemm(args)
         return 0
     if args.op in ("matmul", "matmul_quantize"):
         return bench_matmul(args)

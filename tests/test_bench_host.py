@@ -101,8 +101,9 @@ def test_bad_step_counts_are_refused():
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU exit")
-def test_no_gpu_fails_loudly():
-    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "1", "--warmup", "0"],
+@pytest.mark.parametrize("mode", [[], ["--vendor-gemm"]])
+def test_no_gpu_fails_loudly(mode):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "1", "--warmup", "0"] + mode,
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 1
     assert "no GPU" in r.stderr
