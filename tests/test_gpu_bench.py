@@ -86,3 +86,14 @@ def test_copy_calibration_line():
     assert r.returncode == 0, r.stderr[-2000:]
     d = json.loads(r.stdout.strip().splitlines()[-1])
     assert d["copy_bytes_read"] == d["copy_bytes_written"] == 2 << 30 and d["copy_GBps"] > 0
+
+
+def test_vendor_gemm_line():
+    """--vendor-gemm: the vendor's per-tensor FP8 product at small sizes, one
+    JSON line with its time and rate (context only, not a bench line)."""
+    d = _bench("--vendor-gemm", "--mm", "1024", "1024", "1024", "--steps", "3", "--warmup", "1")
+    v = d["vendor_gemm"]
+    assert (v["M"], v["N"], v["K"]) == (1024, 1024, 1024)
+    assert v["us_per_call"] > 0 and v["TFLOPs"] > 0
+    assert abs(v["TFLOPs"] - 2.0 * 1024 ** 3 / (v["us_per_call"] * 1e-6) / 1e12) < 0.05 * v["TFLOPs"] + 0.1
+    assert d["steps"] == 3 and d["warmup"] == 1 and "metric" not in d
