@@ -341,6 +341,18 @@ def test_outputs_on_caller_stream():
     assert np.array_equal(d.cpu().numpy(), d_ref)
 
 
+def test_binding_uses_the_current_stream():
+    """Without a stream argument the binding enqueues on the device's current
+    stream, whichever way it reads it: the handle it passes equals torch's,
+    on the default stream and inside a stream context."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    assert mxq._stream_handle(None, dev) == torch.cuda.current_stream(dev).cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert mxq._stream_handle(None, dev) == s.cuda_stream != torch.cuda.default_stream(dev).cuda_stream
+    assert mxq._stream_handle(s, dev) == s.cuda_stream
+
+
 def test_concurrent_host_threads():
     """The library keeps no state: host threads calling it at the same time,
     each on its own stream, get the bytes a serial call gives."""
